@@ -1,0 +1,234 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) quantized Mixture-of-Experts FFN block.
+ *
+ * The block (one MoE layer of a Gemma-4-26B-A4B-style model, as the
+ * TurboFieldfare pages describe it):
+ *   - an 8-bit affine router projects each activation row to n_experts logits
+ *     (router kept at 8 bits: ai-heartland review "TurboFieldfareとは",
+ *     system-design summary; rebasdaily article, MLX affine 4-bit paragraph);
+ *   - the top_k experts per row are picked (8 of 128: blog-mushroom article
+ *     "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook", section "Why 26B Fits
+ *     in 2 GB") and weighted by a softmax over the picked logits;
+ *   - each picked expert is a GeGLU FFN over MLX affine 4-bit weights (group
+ *     64 along the input dimension, bf16 scale and bias per group; same
+ *     passages);
+ *   - an always-on shared expert runs beside them and the two paths merge
+ *     (blog-mushroom article, "Why 26B Fits in 2 GB", per-token flow);
+ *   - prefill runs in chunks of rows so that one fetched expert serves every
+ *     row of the chunk routed to it (same section; paperfeed digest
+ *     "drumih/turbo-fieldfare", "How it works").
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to HIP device memory (allocated by the caller,
+ *     e.g. through PyTorch). Host pointers are named *_host.
+ *   - `stream` is a hipStream_t passed as void*. Work is enqueued on it;
+ *     nothing is synchronised unless stated. Pointers must stay valid until
+ *     the stream has reached the enqueued work.
+ *   - The library allocates no device memory. Scratch space comes from the
+ *     caller's workspace `ws` of `ws_bytes` bytes (>= moe_workspace_bytes()).
+ *     The workspace must be zero-filled once before its first use
+ *     (moe_workspace_init); every call leaves its counters at zero again.
+ *     Calls that overlap in time need separate workspaces.
+ *   - Arguments are validated before anything is enqueued; a failing check
+ *     returns a negative moe_status and launches nothing. No C++ exception
+ *     crosses this interface.
+ *   - A slot-table entry that names a blob outside the pool is not followed:
+ *     the kernel records MOE_DEVERR_BAD_SLOT in the library's device error
+ *     word and treats that expert's output as zero; moe_check_device_error()
+ *     reports it.
+ */
+#ifndef QMOE_MOE_H_
+#define QMOE_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,       /* null pointer, bad enum, rows < 0, misaligned pointer */
+  MOE_ERR_UNSUPPORTED_SHAPE = -2, /* a dimension not a multiple of 64, top_k out of range, ... */
+  MOE_ERR_WORKSPACE = -3,         /* ws_bytes < moe_workspace_bytes(...) */
+  MOE_ERR_HIP = -4,               /* a HIP runtime call failed (launch, copy, sync) */
+  MOE_ERR_DEVICE_CHECK = -5       /* a kernel recorded an error in the device error word */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* device error word values (bit flags) */
+#define MOE_DEVERR_BAD_SLOT 1u      /* a slot-table entry named a blob outside the pool */
+#define MOE_DEVERR_BAD_EXPERT_ID 2u /* grouping met an expert id outside [0, n_experts) */
+
+/* Shape of one MoE layer. d_model, d_ff, d_ff_shared: multiples of 64;
+ * n_experts: multiple of 64, at most 256; 1 <= top_k <= min(n_experts, 16);
+ * group must be 64. Gemma-4-26B-A4B-like: {2816, 704, 2112, 128, 8, 64}. */
+typedef struct {
+  int32_t d_model, d_ff, d_ff_shared, n_experts, top_k, group;
+} moe_shape;
+
+/*
+ * One layer's weights, all device memory owned by the caller.
+ *   pool        base of the HBM-resident packed-expert pool: n_blobs blobs of
+ *               blob_stride bytes each (blob_stride >= moe_expert_blob_bytes(),
+ *               multiple of 256). The pages keep 128 fixed-size page-aligned
+ *               expert blobs per layer file and bind sub-regions of them
+ *               (blog-mushroom article, model-file-layout section); here the
+ *               pool holds the blobs of every layer in HBM.
+ *   slot_table  [n_experts] uint32: expert id -> blob index in the pool (the
+ *               per-layer slot table the kernels read; any placement gives the
+ *               same results).
+ *   router_blob packed 8-bit router [n_experts x d_model] (moe_pack_matrix8).
+ *   shared_blob packed shared expert: gate [d_ff_shared x d_model], up (same),
+ *               down [d_model x d_ff_shared], each moe_pack_matrix4, back to back.
+ * An expert blob is gate [d_ff x d_model] | up [d_ff x d_model] |
+ * down [d_model x d_ff], each packed with moe_pack_matrix4, back to back.
+ */
+typedef struct {
+  const uint8_t* pool;
+  uint64_t blob_stride;
+  uint64_t n_blobs;
+  const uint32_t* slot_table;
+  const uint8_t* router_blob;
+  const uint8_t* shared_blob;
+} moe_layer;
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Bytes of workspace any entry point below needs for `rows` activation rows. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t rows);
+
+/* Zero-fills a workspace (enqueued on `stream`). Required once per workspace. */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Packed sizes (bytes) of a 4-bit / 8-bit matrix [rows x cols], of one routed
+ * expert blob (before stride padding), of the shared-expert blob and of the
+ * router blob. 0 if the shape is unsupported. */
+uint64_t moe_matrix4_bytes(int32_t rows, int32_t cols);
+uint64_t moe_matrix8_bytes(int32_t rows, int32_t cols);
+uint64_t moe_expert_blob_bytes(const moe_shape* shape);
+uint64_t moe_shared_blob_bytes(const moe_shape* shape);
+uint64_t moe_router_blob_bytes(const moe_shape* shape);
+
+/* ------------------------------------------------------------------ packer (host, CPU only) */
+
+/*
+ * Canonical (MLX-style) format of a quantized matrix W[rows x cols], w = s*q + b:
+ *   q_host  4-bit: uint8 [rows][cols/2], element 2j in the low nibble of byte j;
+ *           8-bit: uint8 [rows][cols]
+ *   s_host, b_host  uint16 bf16 bit patterns [rows][cols/64]
+ * Device format written to out_host (moe_matrix{4,8}_bytes bytes): tiles of
+ * 64 rows x 64 columns, row-block major then group; each 4-bit tile holds the
+ * codes (2048 B, laid out so that lane r of a wavefront reads row r with
+ * 16-byte loads and one 32-bit word yields four bf16 pairs) followed by the
+ * 64 (s, b) pairs (256 B). rows and cols must be multiples of 64.
+ * The unpackers invert the packers bit-exactly.
+ */
+moe_status moe_pack_matrix4(const uint8_t* q_host, const uint16_t* s_host, const uint16_t* b_host, int32_t rows,
+                            int32_t cols, uint8_t* out_host);
+moe_status moe_pack_matrix8(const uint8_t* q_host, const uint16_t* s_host, const uint16_t* b_host, int32_t rows,
+                            int32_t cols, uint8_t* out_host);
+moe_status moe_unpack_matrix4(const uint8_t* in_host, int32_t rows, int32_t cols, uint8_t* q_host, uint16_t* s_host,
+                              uint16_t* b_host);
+moe_status moe_unpack_matrix8(const uint8_t* in_host, int32_t rows, int32_t cols, uint8_t* q_host, uint16_t* s_host,
+                              uint16_t* b_host);
+
+/* ------------------------------------------------------------------ the block's steps */
+
+/*
+ * Router + top-k + softmax for `rows` rows of x ([rows][d_model], dtype MOE_F32
+ * or MOE_BF16, 16-byte aligned):
+ *   logit[r][e] = sum_i (s*q + b)[e][i] * x[r][i] + logit_offset[e]
+ * accumulated in fp64 (every product exact), so the top-k set is decided on
+ * logits within ~1e-12 of exact. Picks ordered by (logit desc, expert id asc).
+ *   topk_idx [rows][top_k] int32, topk_w [rows][top_k] float (softmax of the
+ *   picked logits), logits [rows][n_experts] double (optional, may be NULL),
+ *   logit_offset [n_experts] float (optional, NULL = 0).
+ */
+moe_status moe_router_topk(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
+                           int32_t rows, const float* logit_offset, int32_t* topk_idx, float* topk_w,
+                           double* logits, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token-to-expert grouping (prefill): the rows*top_k (row, slot) pairs, pair
+ * id = row*top_k + slot, stably sorted by expert id (a counting sort):
+ *   count [n_experts], offset [n_experts+1] (exclusive prefix sum of count),
+ *   perm [rows*top_k] (pair id at each sorted position),
+ *   inv_perm [rows*top_k] (sorted position of each pair). Bit-exact.
+ */
+moe_status moe_group_by_expert(const moe_shape* shape, const int32_t* topk_idx, int32_t rows, int32_t* count,
+                               int32_t* offset, int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * Routed experts for ONE decode row x [d_model]: for each slot j < top_k,
+ *   expert_out[j][:] = W_down (gelu_tanh(W_gate x) * (W_up x)) of expert topk_idx[j]
+ * (unweighted), fp32 [top_k][d_model]. 4-bit dequant is fused into the GEMVs.
+ */
+moe_status moe_expert_ffn_decode(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
+                                 const int32_t* topk_idx, float* expert_out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * Routed experts for a prefill chunk of `rows` rows, grouped by expert
+ * (offset, perm from moe_group_by_expert): for sorted position j with pair
+ * id p = perm[j], row r = p / top_k, expert e = the expert whose range holds j,
+ *   expert_out[j][:] = E_e(x[r]) (unweighted), fp32 [rows*top_k][d_model].
+ * Every expert's weights are read once per 64-row tile of its rows and run
+ * through MFMA on bf16-dequantized tiles.
+ */
+moe_status moe_expert_ffn_prefill_chunk(const moe_shape* shape, const moe_layer* layer, const void* x,
+                                        moe_dtype x_dtype, int32_t rows, const int32_t* offset,
+                                        const int32_t* perm, float* expert_out, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/*
+ * Shared expert + weighted combine:
+ *   y[r][:] = S(x[r]) + sum_{j<top_k} topk_w[r][j] * E_j
+ * where E_j = expert_out[inv_perm[r*top_k + j]] (prefill, inv_perm != NULL) or
+ * expert_out[r*top_k + j] (inv_perm == NULL; decode has rows == 1), summed in
+ * slot order. y fp32 [rows][d_model]. If residual_bf16 is not NULL it is a
+ * bf16 [rows][d_model] in/out buffer: residual = bf16_rne(fp32(residual) + y)
+ * (the residual add between stacked layers).
+ */
+moe_status moe_combine(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
+                       int32_t rows, const float* expert_out, const int32_t* inv_perm, const float* topk_w,
+                       float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole block for one decode row, fused: router + top-k + routed experts +
+ * shared expert + combine (+ optional residual), the same results as the four
+ * calls above. topk_idx/topk_w [top_k], y [d_model]; expert_out [top_k][d_model]
+ * receives the unweighted routed outputs.
+ */
+moe_status moe_layer_decode(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
+                            const float* logit_offset, int32_t* topk_idx, float* topk_w, float* expert_out,
+                            float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole block for a prefill chunk: router + top-k, grouping, grouped expert
+ * GEMMs, shared expert and combine (+ optional residual). Outputs as the
+ * separate calls; count/offset/perm/inv_perm as moe_group_by_expert.
+ */
+moe_status moe_layer_prefill(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
+                             int32_t rows, const float* logit_offset, int32_t* topk_idx, float* topk_w,
+                             int32_t* count, int32_t* offset, int32_t* perm, int32_t* inv_perm,
+                             float* expert_out, float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------ errors */
+
+const char* moe_status_string(moe_status status);
+
+/* Synchronises `stream`, reads and clears the device error word of the
+ * current device. Returns MOE_OK, or MOE_ERR_DEVICE_CHECK with the flags in
+ * *flags (may be NULL). */
+moe_status moe_check_device_error(void* stream, uint32_t* flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_MOE_H_ */

@@ -1,0 +1,94 @@
+// Device-side building blocks shared by the HIP kernels of the quantized MoE block.
+//
+// Packed tile format (written by pack.cpp, read by every kernel):
+//   4-bit matrix [N x K]: tiles of 64 rows x 64 columns (one quantisation group),
+//   tile (nb, g) at byte (nb * K/64 + g) * 2304:
+//     [0, 2048)    codes: half h (columns g*64 + h*32 .. +32) of row r at h*1024 + r*16,
+//                  4 words; word j holds columns c0 = h*32 + 8j .. c0+7, where
+//                  column c0 + 2t sits in bits [4t, 4t+4) and c0 + 2t + 1 in
+//                  bits [16 + 4t, 16 + 4t + 4)  (t = 0..3)
+//     [2048, 2304) (s, b) of row r at 2048 + r*4: s in the low half, b in the high
+//                  half, bf16 bit patterns
+//   8-bit matrix [N x K]: tile (nb, g) at (nb * K/64 + g) * 4352:
+//     [0, 4096)    codes: quarter c (columns g*64 + c*16 .. +16) of row r at c*1024 + r*16
+//     [4096, 4352) (s, b) as above
+// So a wavefront whose lane r owns row r reads 1 KiB contiguous per 16-byte load,
+// and one 32-bit code word masked with 0x000F000F after a shift of 4t gives the
+// bf16 pair (128 + q[c0+2t], 128 + q[c0+2t+1]) once 0x43004300 is OR-ed in
+// (0x4300 | q is the bf16 value 128 + q for q < 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+constexpr int kGroup = 64;
+constexpr int kTile4 = 2304;
+constexpr int kTile4Codes = 2048;
+constexpr int kTile8 = 4352;
+constexpr int kTile8Codes = 4096;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// bf16 pair (128 + q[c0 + 2t], 128 + q[c0 + 2t + 1]) of a packed 4-bit code word
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int t) {
+  return ((w >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// tanh form of GELU (Hendrycks & Gimpel), fp32
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ldg4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// device error word (bit flags, see moe.h); the library is one translation unit
+__device__ uint32_t g_moe_device_error = 0;
+
+__device__ __forceinline__ void flag_device_error(uint32_t bits) { atomicOr(&g_moe_device_error, bits); }
+
+// blob of routed expert `e` through the slot table; nullptr (and the error flag) if out of range
+__device__ __forceinline__ const uint8_t* expert_blob(const uint8_t* pool, uint64_t stride, uint64_t n_blobs,
+                                                      const uint32_t* slot_table, int e) {
+  uint32_t b = slot_table[e];
+  if ((uint64_t)b >= n_blobs) {
+    flag_device_error(1u);
+    return nullptr;
+  }
+  return pool + (uint64_t)b * stride;
+}
+
+// bytes of a packed 4-bit matrix [rows x cols]
+__host__ __device__ __forceinline__ uint64_t m4_bytes(int rows, int cols) {
+  return (uint64_t)(rows / 64) * (uint64_t)(cols / 64) * kTile4;
+}
+
+}  // namespace qmoe

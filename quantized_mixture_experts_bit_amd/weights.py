@@ -1,0 +1,113 @@
+"""Device-resident weights: the packed-expert pool, per-layer slot tables, router
+and shared-expert blobs.
+
+The pages keep every layer's 128 routed experts as fixed-size, page-aligned
+blobs and bind sub-regions of them instead of building one buffer per expert
+(blog-mushroom article "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook",
+model-file-layout section). Here all blobs of all layers live in one
+HBM-resident torch uint8 tensor (the pool, 12.85 GB for 30 x 128 experts at the
+Gemma-4 shape) and each layer has a device slot table (expert id -> blob
+index) that the kernels read. Packing runs on the host through the library's
+C packer; nothing here computes any part of the block.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (as_shape, moe_expert_blob_bytes, moe_layer, moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4,
+               moe_pack_matrix8, moe_router_blob_bytes, moe_shared_blob_bytes)
+
+BLOB_ALIGN = 4096  # blob stride granularity (a page)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def pack_expert_into(shape, expert, out: np.ndarray) -> None:
+    """gate | up | down of one expert (objects with .q/.s/.b) into out[0:blob_bytes]."""
+    d, f = shape.d_model, expert.gate.rows
+    m_gu = moe_matrix4_bytes(f, d)
+    moe_pack_matrix4(expert.gate.q, expert.gate.s, expert.gate.b, out[0:m_gu])
+    moe_pack_matrix4(expert.up.q, expert.up.s, expert.up.b, out[m_gu:2 * m_gu])
+    moe_pack_matrix4(expert.down.q, expert.down.s, expert.down.b, out[2 * m_gu:2 * m_gu + moe_matrix4_bytes(d, f)])
+
+
+def pack_router(shape, router) -> np.ndarray:
+    out = np.empty(moe_router_blob_bytes(as_shape(shape)), dtype=np.uint8)
+    moe_pack_matrix8(router.q, router.s, router.b, out)
+    return out
+
+
+def pack_shared(shape, shared) -> np.ndarray:
+    out = np.empty(moe_shared_blob_bytes(as_shape(shape)), dtype=np.uint8)
+    pack_expert_into(shape, shared, out)
+    return out
+
+
+class DeviceLayer:
+    """One layer's device handles; `c` is the moe_layer struct the C ABI takes."""
+
+    def __init__(self, pool: "ExpertPool", router: torch.Tensor, shared: torch.Tensor, slot_table: torch.Tensor):
+        self.pool = pool
+        self.router = router
+        self.shared = shared
+        self.slot_table = slot_table
+        self.c = moe_layer(pool.buf.data_ptr(), pool.stride, pool.n_blobs, slot_table.data_ptr(),
+                           router.data_ptr(), shared.data_ptr())
+
+
+class ExpertPool:
+    """HBM pool of `n_blobs` expert blobs of `stride` bytes."""
+
+    def __init__(self, shape, n_blobs: int, device="cuda", stride: Optional[int] = None):
+        self.shape = shape
+        blob = moe_expert_blob_bytes(as_shape(shape))
+        self.blob_bytes = blob
+        self.stride = stride or (blob + BLOB_ALIGN - 1) // BLOB_ALIGN * BLOB_ALIGN
+        assert self.stride >= blob and self.stride % 256 == 0
+        self.n_blobs = n_blobs
+        self.device = torch.device(device)
+        self.buf = torch.empty(n_blobs * self.stride, dtype=torch.uint8, device=self.device)
+
+    def load_experts(self, shape, experts: Sequence, blob_index: Sequence[int]) -> None:
+        """Pack `experts` on the host and copy expert i into blob blob_index[i]."""
+        n = len(experts)
+        staging = torch.empty(n * self.stride, dtype=torch.uint8, pin_memory=True)
+        host = staging.numpy()
+        with cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(lambda i: pack_expert_into(shape, experts[i], host[i * self.stride:(i + 1) * self.stride]),
+                        range(n)))
+        idx = list(blob_index)
+        if idx == list(range(idx[0], idx[0] + n)):
+            self.buf[idx[0] * self.stride:(idx[0] + n) * self.stride].copy_(staging)
+        else:
+            dev = staging.to(self.device)
+            for i, b in enumerate(idx):
+                self.buf[b * self.stride:(b + 1) * self.stride].copy_(dev[i * self.stride:(i + 1) * self.stride])
+        torch.cuda.synchronize(self.device)
+
+    def add_layer(self, layer, first_blob: int, placement: Optional[Sequence[int]] = None) -> DeviceLayer:
+        """Upload one canonical layer (router, shared, experts). Expert e goes to blob
+        first_blob + placement[e] (identity placement by default)."""
+        shape = layer.shape
+        E = shape.n_experts
+        place = list(range(E)) if placement is None else list(placement)
+        blobs = [first_blob + p for p in place]
+        self.load_experts(shape, layer.experts, blobs)
+        router = torch.from_numpy(pack_router(shape, layer.router)).to(self.device)
+        shared = torch.from_numpy(pack_shared(shape, layer.shared)).to(self.device)
+        table = torch.tensor(blobs, dtype=torch.int64).to(torch.int32).to(self.device)
+        return DeviceLayer(self, router, shared, table)
+
+
+def upload_layers(shape, layers: List, device="cuda") -> List[DeviceLayer]:
+    """Pool with every expert of every layer, identity placement, layer-major."""
+    E = shape.n_experts
+    pool = ExpertPool(shape, len(layers) * E, device)
+    return [pool.add_layer(L, i * E) for i, L in enumerate(layers)]

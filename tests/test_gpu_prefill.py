@@ -1,0 +1,157 @@
+"""GPU parity of the prefill-chunk path (grouping + grouped MFMA GEMMs + combine)
+against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from _harness import (REL_TOL, check_topk, device, empty_f32, empty_i32, get_layer, rel_err, to_dev_x,
+                      workspace)
+
+pytestmark = pytest.mark.gpu
+q = pytest.importorskip("quantized_mixture_experts_bit_amd")
+
+
+def zipf(shape):
+    return synth.make_zipf_offset(shape, seed=0)
+
+
+@pytest.mark.parametrize("rows,E,k", [(1, 128, 8), (8, 128, 8), (128, 128, 8), (256, 128, 8), (37, 64, 1),
+                                      (200, 256, 16), (3, 64, 16)])
+def test_grouping_bit_exact(rows, E, k):
+    rng = np.random.default_rng(rows * 31 + E + k)
+    skew = np.exp(-np.arange(E) / 8.0)
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=skew / skew.sum()) for _ in range(rows)]).astype(np.int32)
+    shape = q.MoeShape(512, 256, 512, n_experts=E, top_k=k)
+    cnt, off = empty_i32(E), empty_i32(E + 1)
+    perm, inv = empty_i32(rows * k), empty_i32(rows * k)
+    ws = torch.empty(q.moe_workspace_bytes(shape, rows), dtype=torch.uint8, device=device())
+    q.moe_group_by_expert(shape, torch.from_numpy(idx).to(device()), rows, cnt, off, perm, inv, ws)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = O.group_by_expert(idx, E)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(off.cpu().numpy(), ro)
+    np.testing.assert_array_equal(perm.cpu().numpy(), rp)
+    np.testing.assert_array_equal(inv.cpu().numpy(), ri)
+
+
+def run_layer_prefill(shape, dl, x, ws, offset=None, residual=None):
+    rows = x.shape[0]
+    k, d, E = shape.top_k, shape.d_model, shape.n_experts
+    out = dict(idx=empty_i32(rows, k), w=empty_f32(rows, k), cnt=empty_i32(E), off=empty_i32(E + 1),
+               perm=empty_i32(rows * k), inv=empty_i32(rows * k), eo=empty_f32(rows * k, d), y=empty_f32(rows, d))
+    q.moe_layer_prefill(shape, dl.c, to_dev_x(x), rows, offset, out["idx"], out["w"], out["cnt"], out["off"],
+                        out["perm"], out["inv"], out["eo"], out["y"], residual, ws)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in out.items()}
+
+
+PREFILL_CASES = [
+    pytest.param(synth.TINY, 8, "f32", None, None, id="tiny-8rows-f32"),
+    pytest.param(synth.TINY, 8, "f32", synth.Variant(router_scale_log2=-6), None, id="tiny-8rows-f32-soft"),
+    pytest.param(synth.TINY, 65, "bf16", synth.Variant(router_scale_log2=-6), None, id="tiny-65rows-bf16-soft"),
+    pytest.param(synth.TINY, 130, "bf16", None, "zipf", id="tiny-130rows-bf16-zipf"),
+    pytest.param(synth.GEMMA4, 128, "bf16", None, "zipf", id="gemma4-128rows-bf16-zipf"),
+    pytest.param(synth.GEMMA4, 256, "bf16", None, "zipf", id="gemma4-256rows-bf16-zipf"),
+    pytest.param(synth.GEMMA4, 19, "bf16", synth.Variant(router_scale_log2=-6), None, id="gemma4-19rows-soft"),
+]
+
+
+def sample_rows(rows, n=24):
+    if rows <= n:
+        return np.arange(rows)
+    return np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(rows).choice(rows, n - 2, replace=False)]))
+
+
+@pytest.mark.parametrize("shape,rows,dt,variant,skew", PREFILL_CASES)
+def test_layer_prefill(shape, rows, dt, variant, skew):
+    L, ol, dl = get_layer(shape, variant=variant or synth.Variant())
+    x = synth.make_x(shape, rows, seed=11, dtype=dt)
+    off_np = zipf(shape) if skew == "zipf" else None
+    off = None if off_np is None else torch.from_numpy(off_np).to(device())
+    ws = workspace(shape, rows)
+    got = run_layer_prefill(shape, dl, x, ws, offset=off)
+    k = shape.top_k
+    # grouping of the GPU's own picks is exact
+    rc, ro, rp, ri = O.group_by_expert(got["idx"], shape.n_experts)
+    np.testing.assert_array_equal(got["perm"], rp)
+    np.testing.assert_array_equal(got["inv"], ri)
+    sel = sample_rows(rows)
+    ref = O.moe_rows(ol, x[sel], offset=off_np)
+    flagged = check_topk(got["idx"][sel], ref, k)
+    if flagged.any():
+        ref = O.moe_rows(ol, x[sel], offset=off_np, idx=got["idx"][sel])
+    for i, r in enumerate(sel):
+        assert rel_err(got["y"][r], ref["y"][i]) <= REL_TOL, "row %d" % r
+        for j in range(k):
+            pos = got["inv"][r * k + j]
+            e = rel_err(got["eo"][pos], ref["expert_out"][i, j])
+            assert e <= REL_TOL, "row %d slot %d expert %d: %g" % (r, j, got["idx"][r, j], e)
+    assert q.moe_check_device_error() == 0
+    if skew == "zipf" and shape is synth.GEMMA4:
+        # the skew really makes experts repeat across rows
+        assert (got["cnt"] > 0).sum() < 60 and got["cnt"].max() >= rows // 2
+
+
+def test_prefill_chunk_split_calls_match_fused():
+    shape = synth.GEMMA4
+    L, ol, dl = get_layer(shape)
+    rows, k, d, E = 40, shape.top_k, shape.d_model, shape.n_experts
+    x = synth.make_x(shape, rows, seed=12, dtype="bf16")
+    xd = to_dev_x(x)
+    ws = workspace(shape, rows)
+    fused = run_layer_prefill(shape, dl, x, ws)
+    idx, w = empty_i32(rows, k), empty_f32(rows, k)
+    q.moe_router_topk(shape, dl.c, xd, rows, None, idx, w, None, ws)
+    cnt, off, perm, inv = empty_i32(E), empty_i32(E + 1), empty_i32(rows * k), empty_i32(rows * k)
+    q.moe_group_by_expert(shape, idx, rows, cnt, off, perm, inv, ws)
+    eo, y = empty_f32(rows * k, d), empty_f32(rows, d)
+    q.moe_expert_ffn_prefill_chunk(shape, dl.c, xd, rows, off, perm, eo, ws)
+    q.moe_combine(shape, dl.c, xd, rows, eo, inv, w, y, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), fused["idx"])
+    assert np.array_equal(eo.cpu().numpy(), fused["eo"])
+    assert np.array_equal(y.cpu().numpy(), fused["y"])
+
+
+def test_prefill_rows_match_decode():
+    """Row r of a prefill chunk and a decode call on x_r agree within the tolerance."""
+    shape = synth.GEMMA4
+    L, ol, dl = get_layer(shape)
+    rows = 24
+    x = synth.make_x(shape, rows, seed=13, dtype="bf16")
+    ws = workspace(shape, rows)
+    got = run_layer_prefill(shape, dl, x, ws)
+    k, d = shape.top_k, shape.d_model
+    for r in (0, 7, 23):
+        idx, w, eo, y = empty_i32(k), empty_f32(k), empty_f32(k, d), empty_f32(d)
+        q.moe_layer_decode(shape, dl.c, to_dev_x(x[r:r + 1]), None, idx, w, eo, y, None, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), got["idx"][r])
+        assert rel_err(got["y"][r], y.cpu().numpy()) <= REL_TOL
+
+
+def test_empty_chunk_is_a_no_op():
+    shape = synth.TINY
+    L, ol, dl = get_layer(shape)
+    ws = workspace(shape, 1)
+    x = torch.zeros(1, shape.d_model, dtype=torch.bfloat16, device=device())
+    y = torch.full((1, shape.d_model), 7.0, device=device())
+    k, E = shape.top_k, shape.n_experts
+    q.moe_layer_prefill(shape, dl.c, x, 0, None, empty_i32(1, k), empty_f32(1, k), empty_i32(E), empty_i32(E + 1),
+                        empty_i32(k), empty_i32(k), empty_f32(k, shape.d_model), y, None, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_prefill_deterministic():
+    shape = synth.GEMMA4
+    L, ol, dl = get_layer(shape)
+    x = synth.make_x(shape, 128, seed=14, dtype="bf16")
+    off = torch.from_numpy(zipf(shape)).to(device())
+    ws = workspace(shape, 128)
+    a = run_layer_prefill(shape, dl, x, ws, offset=off)
+    b = run_layer_prefill(shape, dl, x, ws, offset=off)
+    for n in a:
+        assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), n
