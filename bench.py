@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MoE FFN block on one MI355X.
+
+Metric: MoE-layer tokens/s at decode batch 1 (one Gemma-4-26B-A4B-like layer:
+d_model 2816, 128 experts of d_ff 704 with 4-bit affine group-64 weights, shared
+expert d_ff 2112, 8-bit router, top-8), with the fraction of the HBM roofline
+on active-expert bytes. The 128-row prefill chunk (Zipf-skewed routing) is
+measured in the same run and reported under "prefill" with its roofline and
+MFMA utilisation; the 30-layer stacks under "stack" when --stack is given.
+
+Inputs are synthetic and seeded (see synth/): every step uses a different layer
+of a pool of independently drawn layers and a fresh activation row, so the
+weights a step touches are not resident in the 256 MB Infinity Cache from the
+previous step. All inputs are in HBM before the timed region. Steps are
+captured in HIP graphs (one graph = one pass over the rotation) and replayed.
+
+One JSON line on stdout; progress on stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_F16_PEAK = 2.5e15     # flop/s, dense fp16/bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(shape):
+    """Algorithmic HBM bytes of one decode token-layer: router + top_k experts +
+    shared expert weights, x in (bf16) and y out (fp32)."""
+    import quantized_mixture_experts_bit_amd as q
+    s = q.as_shape(shape)
+    return (q.moe_router_blob_bytes(s) + shape.top_k * q.moe_expert_blob_bytes(s) + q.moe_shared_blob_bytes(s)
+            + 2 * shape.d_model + 4 * shape.d_model)
+
+
+def prefill_roofline(shape, counts, rows):
+    """Ideal time of one prefill chunk: per GEMM group max(bytes / HBM, flops / MFMA)."""
+    import quantized_mixture_experts_bit_amd as q
+    s = q.as_shape(shape)
+    d, f, fs = shape.d_model, shape.d_ff, shape.d_ff_shared
+    t = 0.0
+    flops = 0.0
+    nbytes = 0.0
+    for c in counts:
+        if c > 0:
+            fl = 2.0 * c * 3 * f * d
+            by = q.moe_expert_blob_bytes(s)
+            t += max(by / HBM_PEAK, fl / MFMA_F16_PEAK)
+            flops += fl
+            nbytes += by
+    fl = 2.0 * rows * 3 * fs * d
+    by = q.moe_shared_blob_bytes(s)
+    t += max(by / HBM_PEAK, fl / MFMA_F16_PEAK)
+    flops += fl
+    nbytes += by
+    rb = q.moe_router_blob_bytes(s) + rows * d * 2 + rows * d * 4
+    t += rb / HBM_PEAK
+    nbytes += rb
+    return t, flops, nbytes
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=600, help="timed decode steps (prefill: steps/10 chunks)")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed graph replays before timing")
+    ap.add_argument("--layers", type=int, default=16, help="distinct seeded layers in the rotation pool")
+    ap.add_argument("--prefill-rows", type=int, default=128)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the oracle's timed CPU sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import quantized_mixture_experts_bit_amd as q
+    from quantized_mixture_experts_bit_amd.weights import ExpertPool
+
+    dev = torch.device("cuda:0")
+    shape = synth.GEMMA4
+    E, k, d = shape.n_experts, shape.top_k, shape.d_model
+    L = args.layers
+
+    # ---------------------------------------------------------------- weights
+    t0 = time.time()
+    pool = ExpertPool(shape, L * E, dev)
+    layers_c = []
+    dls = []
+    for i in range(L):
+        lay = synth.make_layer(shape, seed=0, layer=i)
+        dls.append(pool.add_layer(lay, i * E))
+        if i == 0:
+            layers_c.append(lay)  # layer 0 kept for the CPU baseline
+        del lay
+    log("pool: %d layers x %d experts, %.2f GB, built in %.1f s" % (L, E, pool.buf.numel() / 1e9,
+                                                                      time.time() - t0))
+
+    # ---------------------------------------------------------------- decode
+    steps_per_graph = 4 * L
+    n_x = steps_per_graph
+    xs = torch.from_numpy(synth.make_x(shape, n_x, seed=1, dtype="bf16")).view(torch.bfloat16).to(dev)
+    ws = torch.empty(q.moe_workspace_bytes(shape, max(1, args.prefill_rows)), dtype=torch.uint8, device=dev)
+    q.moe_workspace_init(ws)
+    idx = torch.empty(n_x, k, dtype=torch.int32, device=dev)
+    w = torch.empty(n_x, k, dtype=torch.float32, device=dev)
+    eo = torch.empty(k, d, dtype=torch.float32, device=dev)
+    y = torch.empty(n_x, d, dtype=torch.float32, device=dev)
+
+    def decode_step(i):
+        q.moe_layer_decode(shape, dls[i % L].c, xs[i:i + 1], None, idx[i], w[i], eo, y[i], None, ws)
+
+    # eager pass (also warms up the code objects)
+    for i in range(steps_per_graph):
+        decode_step(i)
+    torch.cuda.synchronize()
+    assert q.moe_check_device_error() == 0
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(steps_per_graph):
+            decode_step(i)
+    replays = max(1, args.steps // steps_per_graph)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    dec_steps = replays * steps_per_graph
+    dec_ms = ev0.elapsed_time(ev1) / dec_steps
+    dec_tok_s = 1000.0 / dec_ms
+    dbytes = decode_bytes(shape)
+    dec_bw = dbytes / (dec_ms * 1e-3)
+    log("decode: %d steps, %.2f us/step, %.0f tok/s, %.2f TB/s on active bytes (%.1f%% of 8 TB/s)"
+        % (dec_steps, dec_ms * 1e3, dec_tok_s, dec_bw / 1e12, 100 * dec_bw / HBM_PEAK))
+
+    # ---------------------------------------------------------------- prefill
+    prefill = None
+    if not args.no_prefill:
+        R = args.prefill_rows
+        n_chunks = L
+        zipf = [torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=i)).to(dev) for i in range(L)]
+        xp = [torch.from_numpy(synth.make_x(shape, R, seed=2, stream=i, dtype="bf16")).view(torch.bfloat16).to(dev)
+              for i in range(n_chunks)]
+        pidx = torch.empty(n_chunks, R, k, dtype=torch.int32, device=dev)
+        pw = torch.empty(n_chunks, R, k, dtype=torch.float32, device=dev)
+        cnt = torch.empty(n_chunks, E, dtype=torch.int32, device=dev)
+        off = torch.empty(n_chunks, E + 1, dtype=torch.int32, device=dev)
+        perm = torch.empty(n_chunks, R * k, dtype=torch.int32, device=dev)
+        inv = torch.empty(n_chunks, R * k, dtype=torch.int32, device=dev)
+        peo = torch.empty(R * k, d, dtype=torch.float32, device=dev)
+        py = torch.empty(n_chunks, R, d, dtype=torch.float32, device=dev)
+
+        def prefill_step(i):
+            q.moe_layer_prefill(shape, dls[i % L].c, xp[i], R, zipf[i % L], pidx[i], pw[i], cnt[i], off[i], perm[i],
+                                inv[i], peo, py[i], None, ws)
+
+        for i in range(n_chunks):
+            prefill_step(i)
+        torch.cuda.synchronize()
+        assert q.moe_check_device_error() == 0
+        counts = cnt.cpu().numpy()
+        gp = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gp, stream=cap):
+            for i in range(n_chunks):
+                prefill_step(i)
+        p_replays = max(1, args.steps // 10 // n_chunks)
+        for _ in range(args.warmup):
+            gp.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(p_replays):
+            gp.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        p_ms = ev0.elapsed_time(ev1) / (p_replays * n_chunks)
+        ideal = [prefill_roofline(shape, counts[i], R) for i in range(n_chunks)]
+        t_ideal = float(np.mean([t for t, _, _ in ideal]))
+        flops = float(np.mean([fl for _, fl, _ in ideal]))
+        nbytes = float(np.mean([by for _, _, by in ideal]))
+        distinct = float(np.mean((counts > 0).sum(1)))
+        prefill = {
+            "workload": "prefill chunk of %d rows, same layer shape, Zipf(1.1)-skewed router logits" % R,
+            "metric": "MoE-layer tokens/s (prefill chunk %d)" % R,
+            "value": R / (p_ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": p_ms,
+            "chunks": p_replays * n_chunks,
+            "roofline": {"bound": "sum over GEMMs of max(bytes/HBM, flops/MFMA)", "ideal_ms": t_ideal * 1e3,
+                         "frac": t_ideal / (p_ms * 1e-3)},
+            "mfma_util": flops / (p_ms * 1e-3) / MFMA_F16_PEAK,
+            "achieved_tflops": flops / (p_ms * 1e-3) / 1e12,
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "distinct_experts_mean": distinct,
+            "rows_per_expert_max_mean": float(np.mean(counts.max(1))),
+            # rows routed to an expert -> how many (chunk, expert) pairs had that many
+            "rows_per_expert_hist": {str(b): int(v) for b, v in
+                                     zip(*np.unique(counts[counts > 0], return_counts=True))},
+        }
+        log("prefill: %d rows, %.1f us/chunk, %.0f tok/s, roofline frac %.3f, MFMA util %.3f, %.1f distinct experts"
+            % (R, p_ms * 1e3, prefill["value"], prefill["roofline"]["frac"], prefill["mfma_util"], distinct))
+
+    # ---------------------------------------------------------------- CPU baseline (the oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        O.set_threads(cores)
+        ol = O.OracleLayer(layers_c[0])
+        xc = synth.make_x(shape, args.cpu_rows, seed=3, dtype="bf16")
+        t = time.time()
+        O.moe_rows(ol, xc, want=("idx", "p", "y"))
+        dt = time.time() - t
+        cpu = {"value": args.cpu_rows / dt, "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
+               "sample": "%d independent decode rows of the same layer shape (fp64 C oracle, OpenMP over rows), "
+                         "%.1f s wall" % (args.cpu_rows, dt)}
+        log("cpu oracle: %d rows in %.1f s on %d threads -> %.2f tok/s" % (args.cpu_rows, dt, O.threads(),
+                                                                           cpu["value"]))
+
+    out = {
+        "metric": "MoE-layer tokens/s (decode bs=1)",
+        "value": dec_tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": dec_steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations, 4-bit/8-bit affine weights, fp32 accumulate (router fp64)",
+        "data": "synthetic (seeded random weights and activations of the named shapes)",
+        "config": {
+            "workload": "decode, batch 1 token, one MoE layer: d_model 2816, 128 experts (gate/up 2816x704, "
+                        "down 704x2816, 4-bit affine g64 bf16 scale+bias), shared expert d_ff 2112, 8-bit router "
+                        "128x2816, top-8 softmax, GeGLU; rotating over %d seeded layers" % L,
+            "global_batch": 1,
+            "seq_len": 1,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "moe_layer_decode (router + top-k, gate/up+GeGLU, down+combine launches)",
+            "achieved": dec_bw / 1e9,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": dec_bw / HBM_PEAK,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dbytes,
+        },
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -75,7 +75,17 @@ def lib():
         _lib.oracle_group_by_expert.argtypes = [P(C.c_int32), C.c_int32, C.c_int32, C.c_int32,
                                                 P(C.c_int32), P(C.c_int32), P(C.c_int32), P(C.c_int32)]
         _lib.oracle_residual_bf16.argtypes = [P(C.c_uint16), P(C.c_float), C.c_int64, P(C.c_uint16)]
+        _lib.oracle_set_threads.argtypes = [C.c_int32]
+        _lib.oracle_threads.restype = C.c_int32
     return _lib
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
 
 
 def _ptr(a: Optional[np.ndarray], ctype=C.c_double):

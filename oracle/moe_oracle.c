@@ -249,3 +249,13 @@ void oracle_residual_bf16(const uint16_t* x, const float* y, int64_t n, uint16_t
     out[i] = (uint16_t)(u >> 16);
   }
 }
+
+/* thread control for timing runs (OpenMP splits rows only) */
+#ifdef _OPENMP
+#include <omp.h>
+void oracle_set_threads(int32_t n) { omp_set_num_threads(n); }
+int32_t oracle_threads(void) { return omp_get_max_threads(); }
+#else
+void oracle_set_threads(int32_t n) { (void)n; }
+int32_t oracle_threads(void) { return 1; }
+#endif

@@ -70,6 +70,26 @@ __device__ __forceinline__ T wave_sum(T v) {
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t ldg4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
+// Cross-workgroup hand-off inside one kernel without cache flushes. The 8 XCDs
+// of the chip each have their own L2, which is not coherent with the others for
+// ordinary accesses; an agent-scope fence therefore writes back and invalidates
+// the whole local L2 (buffer_wbl2 / buffer_inv), and with hundreds of
+// workgroups fencing those serialise. Instead, data handed to another
+// workgroup is stored and loaded with agent-scope relaxed atomics (sc1: write
+// through to / read from the coherence point), the producer waits for its
+// stores to complete (vmcnt(0)) before it bumps the arrival counter, and the
+// consumer that sees the final count reads with sc1 loads.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t arrive(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // device error word (bit flags, see moe.h); the library is one translation unit
 __device__ uint32_t g_moe_device_error = 0;
 

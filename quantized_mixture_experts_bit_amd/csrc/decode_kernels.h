@@ -189,23 +189,27 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs A, const XT* _
   }
   const float r = reduce_waves4(acc, red, wave, lane);
   const size_t pbase = ((size_t)(slot * 2 + mat) * A.nbmax + nb) * A.P;
-  if (wave == 0) A.gu_partial[(pbase + part) * 64 + lane] = r;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&A.gu_count[slot * A.nbmax + nb], 1u);
-    last = (old == (uint32_t)(2 * A.P - 1));
+  if (wave == 0) {
+    st_agent(&A.gu_partial[(pbase + part) * 64 + lane], r);
+    wait_mem();
+    if (lane == 0) last = (arrive(&A.gu_count[slot * A.nbmax + nb]) == (uint32_t)(2 * A.P - 1));
   }
   __syncthreads();
   if (!last) return;
-  __threadfence();
   if (wave == 0) {
     const size_t gb = ((size_t)(slot * 2 + 0) * A.nbmax + nb) * A.P;
     const size_t ub = ((size_t)(slot * 2 + 1) * A.nbmax + nb) * A.P;
+    float gv[8], uv[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      gv[p] = p < A.P ? ld_agent(&A.gu_partial[(gb + p) * 64 + lane]) : 0.0f;
+      uv[p] = p < A.P ? ld_agent(&A.gu_partial[(ub + p) * 64 + lane]) : 0.0f;
+    }
     float gs = 0.0f, us = 0.0f;
-    for (int p = 0; p < A.P; ++p) {
-      gs += __builtin_nontemporal_load(&A.gu_partial[(gb + p) * 64 + lane]);
-      us += __builtin_nontemporal_load(&A.gu_partial[(ub + p) * 64 + lane]);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      gs += gv[p];
+      us += uv[p];
     }
     const float h = gelu_tanh(gs) * us;
     const uint32_t hi = f32_to_bf16_bits(h);
@@ -262,26 +266,30 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs A) {
   const float r = reduce_waves4(acc, red, wave, lane);
   const int n = nb * 64 + lane;
   if (wave == 0) {
-    if (slot < A.top_k)
-      A.expert_out[(size_t)slot * A.d + n] = r;
-    else
-      A.shared_part[(size_t)part * A.d + n] = r;
+    float* dst = slot < A.top_k ? &A.expert_out[(size_t)slot * A.d + n] : &A.shared_part[(size_t)part * A.d + n];
+    if (A.combine_arrivals == 0) {
+      *dst = r;
+    } else {
+      st_agent(dst, r);
+      wait_mem();
+      if (lane == 0) last = (arrive(&A.dn_count[nb]) == (uint32_t)(A.combine_arrivals - 1));
+    }
   }
   if (A.combine_arrivals == 0) return;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&A.dn_count[nb], 1u);
-    last = (old == (uint32_t)(A.combine_arrivals - 1));
-  }
   __syncthreads();
   if (!last) return;
-  __threadfence();
   if (wave == 0) {
+    float sp[8], ev[16];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) sp[p] = p < A.Ps ? ld_agent(&A.shared_part[(size_t)p * A.d + n]) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ev[k] = k < A.top_k ? ld_agent(&A.expert_out[(size_t)k * A.d + n]) : 0.0f;
     float yv = 0.0f;
-    for (int p = 0; p < A.Ps; ++p) yv += __builtin_nontemporal_load(&A.shared_part[(size_t)p * A.d + n]);
-    for (int k = 0; k < A.top_k; ++k)
-      yv = fmaf(A.topk_w[k], __builtin_nontemporal_load(&A.expert_out[(size_t)k * A.d + n]), yv);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) yv += sp[p];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < A.top_k) yv = fmaf(A.topk_w[k], ev[k], yv);
     A.y[n] = yv;
     if (A.residual) {
       const float t = bf16_to_f32(A.residual[n]) + yv;

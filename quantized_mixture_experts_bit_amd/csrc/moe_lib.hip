@@ -10,7 +10,8 @@
 #include "common.h"
 #include "decode_kernels.h"
 #include "moe.h"
-#include "prefill_kernels.h"
+#include "group_kernels.h"
+#include "prefill_gemm.h"
 #include "router_kernels.h"
 
 using namespace qmoe;
@@ -28,6 +29,8 @@ bool shape_ok(const moe_shape* s) {
   if (s->group != 64) return false;
   if (s->d_model <= 0 || s->d_ff <= 0 || s->d_ff_shared <= 0) return false;
   if (s->d_model % 64 || s->d_ff % 64 || s->d_ff_shared % 64) return false;
+  // reduction parts of the decode GEMVs: at most 8 of 12 groups each
+  if (s->d_model > 8 * kGroupsPerPart * 64 || s->d_ff_shared > 8 * kGroupsPerPart * 64) return false;
   if (s->n_experts < 64 || s->n_experts > 256 || s->n_experts % 64) return false;
   if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->n_experts) return false;
   return true;
@@ -35,17 +38,18 @@ bool shape_ok(const moe_shape* s) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// router split: groups and rows per workgroup
+// router split: rows per workgroup and reduction splits (16 groups each)
 struct RouterCfg {
-  int gpw, rpw, nsplit;
+  int rpw, nsplit;
 };
 RouterCfg router_cfg(const moe_shape* s, int rows) {
   RouterCfg c;
-  c.gpw = rows <= 4 ? 1 : 2;
   c.rpw = rows <= 4 ? 1 : 2;
-  c.nsplit = cdiv(s->d_model / 64, c.gpw);
+  c.nsplit = cdiv(s->d_model / 64, kRouterGPB);
   return c;
 }
+// most activation rows a call can take: rows * top_k < 65536
+inline int max_rows(const moe_shape* s) { return 65535 / s->top_k; }
 
 struct DecodeCfg {
   int P, Ps, fmax, nbmax;
@@ -59,10 +63,12 @@ DecodeCfg decode_cfg(const moe_shape* s) {
   return c;
 }
 
-// Workspace layout. Counters first (zeroed once, left at zero by every call).
+// Workspace layout. The counters come first in a region whose size depends on
+// the shape only (zeroed once, left at zero by every call), so layouts for
+// different row counts never place a counter where another call kept data.
 struct Ws {
-  size_t gu_count, dn_count, router_partial, gu_partial, h_hi, h_lo, h_gsum, shared_part, pf_H, pf_Hs,
-      pf_shared_out, total;
+  size_t rt_count, gu_count, dn_count, router_partial, gu_partial, h_hi, h_lo, h_gsum, shared_part, pf_H,
+      pf_Hs, pf_shared_out, pf_xscale, pf_hmax, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -76,6 +82,7 @@ Ws ws_layout(const moe_shape* s, int rows) {
     o = align256(o + bytes);
     return at;
   };
+  w.rt_count = take(sizeof(uint32_t) * max_rows(s));
   w.gu_count = take(sizeof(uint32_t) * (k + 1) * dc.nbmax);
   w.dn_count = take(sizeof(uint32_t) * (d / 64));
   w.router_partial = take(sizeof(double) * rc.nsplit * R * s->n_experts);
@@ -84,9 +91,11 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.h_lo = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
   w.h_gsum = take(sizeof(float) * (size_t)(k + 1) * dc.nbmax);
   w.shared_part = take(sizeof(float) * (size_t)dc.Ps * d);
-  w.pf_H = take(sizeof(uint16_t) * R * k * s->d_ff);
-  w.pf_Hs = take(sizeof(uint16_t) * R * s->d_ff_shared);
+  w.pf_H = take(sizeof(float) * R * k * s->d_ff);
+  w.pf_Hs = take(sizeof(float) * R * s->d_ff_shared);
   w.pf_shared_out = take(sizeof(float) * R * d);
+  w.pf_xscale = take(sizeof(float) * R);
+  w.pf_hmax = take(sizeof(uint32_t) * R * (k + 1));
   w.total = o;
   return w;
 }
@@ -131,12 +140,14 @@ void launch_router(const moe_shape* s, const moe_layer* L, const XT* x, int rows
   const RouterCfg rc = router_cfg(s, rows);
   const Ws W = ws_layout(s, rows);
   double* part = at<double>(ws, W.router_partial);
+  uint32_t* cnt = at<uint32_t>(ws, W.rt_count);
   dim3 grid(s->n_experts / 64, rc.nsplit, cdiv(rows, rc.rpw));
   if (rc.rpw == 1)
-    k_router_partial<XT, 1, 1><<<grid, 64, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, part);
+    k_router<XT, 1><<<grid, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, s->top_k, rc.nsplit,
+                                          off, part, cnt, idx, w, logits);
   else
-    k_router_partial<XT, 2, 2><<<grid, 64, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, part);
-  k_topk<<<rows, 64, 0, st>>>(part, rc.nsplit, rows, s->n_experts, s->top_k, off, idx, w, logits);
+    k_router<XT, 2><<<grid, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, s->top_k, rc.nsplit,
+                                          off, part, cnt, idx, w, logits);
 }
 
 DecodeArgs decode_args(const moe_shape* s, const moe_layer* L, const int32_t* idx, void* ws, float* expert_out,
@@ -209,15 +220,18 @@ PrefillArgs prefill_args(const moe_shape* s, const moe_layer* L, int rows, const
   const int P = rows * s->top_k;
   A.routed_mtiles = cdiv(P, 64) + std::min(s->n_experts, P);
   A.shared_mtiles = cdiv(rows, 64);
-  A.H = at<uint16_t>(ws, W.pf_H);
-  A.Hs = at<uint16_t>(ws, W.pf_Hs);
+  A.H = at<float>(ws, W.pf_H);
+  A.Hs = at<float>(ws, W.pf_Hs);
   A.expert_out = expert_out;
   A.shared_out = at<float>(ws, W.pf_shared_out);
+  A.xscale = at<float>(ws, W.pf_xscale);
+  A.hmax = at<uint32_t>(ws, W.pf_hmax);
   return A;
 }
 
 template <typename XT>
 void launch_prefill(const PrefillArgs& A, const XT* x, bool routed, bool shared, hipStream_t st) {
+  k_prefill_scales<XT><<<A.rows, 256, 0, st>>>(x, A.rows, A.d, A.top_k, const_cast<float*>(A.xscale), A.hmax);
   if (routed) k_prefill_gateup<XT><<<A.routed_mtiles * (A.f / 32), 256, 0, st>>>(A, x, 0);
   if (shared) k_prefill_gateup<XT><<<A.shared_mtiles * (A.fs / 32), 256, 0, st>>>(A, x, 1);
   if (routed) k_prefill_down<<<A.routed_mtiles * (A.d / 64), 256, 0, st>>>(A, 0);
