@@ -261,7 +261,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "moe_layer_decode (router + top-k, gate/up+GeGLU, down+combine launches)",
+            "kernel": "k_decode_fused (moe_layer_decode: the whole block for one row in one launch)",
             "achieved": dec_bw / 1e9,
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",

@@ -60,7 +60,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* device error word values (bit flags) */
 #define MOE_DEVERR_BAD_SLOT 1u      /* a slot-table entry named a blob outside the pool */
-#define MOE_DEVERR_BAD_EXPERT_ID 2u /* grouping met an expert id outside [0, n_experts) */
+#define MOE_DEVERR_BAD_EXPERT_ID 2u /* an expert id outside [0, n_experts) (e.g. NaN logits) */
+#define MOE_DEVERR_SYNC_TIMEOUT 4u  /* a fused-decode wait gave up; re-initialise the workspace */
 
 /* Shape of one MoE layer. d_model, d_ff, d_ff_shared: multiples of 64;
  * n_experts: multiple of 64, at most 256; 1 <= top_k <= min(n_experts, 16);

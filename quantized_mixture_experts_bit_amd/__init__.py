@@ -29,6 +29,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED_SHAPE, MOE_ERR_WORKSPACE, MOE_E
     0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
 MOE_DEVERR_BAD_SLOT = 1
+MOE_DEVERR_BAD_EXPERT_ID = 2
+MOE_DEVERR_SYNC_TIMEOUT = 4
 
 
 class MoeError(RuntimeError):

@@ -53,17 +53,18 @@ struct VecSplit {  // precomputed hi/lo bf16 arrays (the GeGLU output h)
 template <typename V>
 __device__ __forceinline__ float group_dot(const V& v, int g, uint4 qa, uint4 qb, uint32_t sbw, float Vg) {
   const uint32_t words[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-  float a = 0.0f;
+  float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four independent dot2 chains
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int pbase = g * 32 + (j >> 2) * 16 + (j & 3) * 4;  // pair index of column g*64 + h*32 + 8*jj
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t p = nib_pair(words[j], t);
-      a = dot2(p, v.hi(pbase + t), a);
-      if (V::kLo) a = dot2(p, v.lo(pbase + t), a);
+      acc4[t] = dot2(p, v.hi(pbase + t), acc4[t]);
+      if (V::kLo) acc4[t] = dot2(p, v.lo(pbase + t), acc4[t]);
     }
   }
+  const float a = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   const float s = bf16_lo(sbw), b = bf16_hi(sbw);
   return fmaf(s, a, fmaf(-128.0f, s, b) * Vg);
 }
@@ -127,7 +128,7 @@ struct DecodeArgs {
   const uint32_t* slot_table;
   const int32_t* topk_idx;
   const uint8_t* shared_blob;
-  int d, f, fs, top_k;
+  int d, f, fs, top_k, n_experts;
   int P;             // reduction parts of gate/up
   int Ps;            // reduction parts of the shared down
   int routed_units;  // workgroups for routed work (0 if none)
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs A, const XT* _
     slot = u / per;
     u -= slot * per;
     F = A.f;
-    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot]);
+    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot], A.n_experts);
   } else {
     u -= A.routed_units;
     slot = A.top_k;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs A) {
     F = A.f;
     g0 = 0;
     g1 = F / kGroup;
-    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot]);
+    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot], A.n_experts);
   } else {
     u -= A.routed_units;
     slot = A.top_k;

@@ -8,6 +8,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "decode_fused.h"
 #include "decode_kernels.h"
 #include "moe.h"
 #include "group_kernels.h"
@@ -67,8 +68,8 @@ DecodeCfg decode_cfg(const moe_shape* s) {
 // the shape only (zeroed once, left at zero by every call), so layouts for
 // different row counts never place a counter where another call kept data.
 struct Ws {
-  size_t rt_count, gu_count, dn_count, router_partial, gu_partial, h_hi, h_lo, h_gsum, shared_part, pf_H,
-      pf_Hs, pf_shared_out, pf_xscale, pf_hmax, total;
+  size_t rt_count, gu_count, dn_count, fused_sync, router_partial, fused_rt, gu_partial, h_hi, h_lo, h_gsum,
+      shared_part, pf_H, pf_Hs, pf_shared_out, pf_xscale, pf_hmax, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -85,7 +86,9 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.rt_count = take(sizeof(uint32_t) * max_rows(s));
   w.gu_count = take(sizeof(uint32_t) * (k + 1) * dc.nbmax);
   w.dn_count = take(sizeof(uint32_t) * (d / 64));
+  w.fused_sync = take(sizeof(uint32_t) * kFusedSyncWords);
   w.router_partial = take(sizeof(double) * rc.nsplit * R * s->n_experts);
+  w.fused_rt = take(sizeof(double) * cdiv(s->d_model / 64, 4) * s->n_experts);
   w.gu_partial = take(sizeof(float) * (size_t)(k + 1) * 2 * dc.nbmax * dc.P * 64);
   w.h_hi = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
   w.h_lo = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
@@ -166,6 +169,7 @@ DecodeArgs decode_args(const moe_shape* s, const moe_layer* L, const int32_t* id
   A.f = s->d_ff;
   A.fs = s->d_ff_shared;
   A.top_k = s->top_k;
+  A.n_experts = s->n_experts;
   A.P = dc.P;
   A.Ps = dc.Ps;
   A.fmax = dc.fmax;
@@ -197,6 +201,55 @@ void launch_decode_down(DecodeArgs A, bool routed, bool shared, bool combine, hi
   const int shared_units = shared ? (A.d / 64) * A.Ps : 0;
   A.combine_arrivals = combine ? (shared ? A.Ps : 0) + (routed ? A.top_k : 0) : 0;
   k_decode_down<kDecodeGW><<<A.routed_units + shared_units, 256, 0, st>>>(A);
+}
+
+// Workgroups of the fused decode kernel the device can hold at once (per device, cached).
+template <typename XT>
+int fused_capacity() {
+  static int cap[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cap[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<XT>, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cap[dev] = std::max(1, per_cu * cus);
+  }
+  return cap[dev];
+}
+
+// One persistent launch for the whole decode row, when the grid fits on the chip;
+// returns false (nothing launched) otherwise.
+template <typename XT>
+bool launch_decode_fused(const moe_shape* s, const moe_layer* L, const XT* x, const float* off, int32_t* idx,
+                         float* w, float* expert_out, float* y, uint16_t* residual, void* ws, hipStream_t st) {
+  // h of one routed slot must fit the workgroup's LDS buffer (12 groups); the
+  // GeGLU rebuild and the combine read at most 4 reduction parts
+  const DecodeCfg dc = decode_cfg(s);
+  if (s->d_ff / 64 > 12 || dc.P > 4 || dc.Ps > 4) return false;
+  const Ws W = ws_layout(s, 1);
+  FusedArgs F;
+  memset(&F, 0, sizeof F);
+  F.A = decode_args(s, L, idx, ws, expert_out, w, y, residual);
+  F.router_blob = L->router_blob;
+  F.offset = off;
+  F.rt_partial = at<double>(ws, W.fused_rt);
+  F.idx_out = idx;
+  F.w_out = w;
+  F.sync = at<uint32_t>(ws, W.fused_sync);
+  F.n_experts = s->n_experts;
+  F.nsplit_r = cdiv(s->d_model / 64, 4);
+  const DecodeArgs& A = F.A;
+  F.n_rt = (s->n_experts / 64) * F.nsplit_r;
+  F.n_sg = 2 * (A.fs / 64) * A.P;
+  F.n_rg = A.top_k * 2 * (A.f / 64) * A.P;
+  F.n_sd = (A.d / 64) * A.Ps;
+  F.n_rd = A.top_k * (A.d / 64);
+  const int grid = F.n_rt + F.n_sg + F.n_rg + F.n_sd + F.n_rd;
+  if (grid > fused_capacity<XT>()) return false;
+  k_decode_fused<XT><<<grid, 256, 0, st>>>(F, x);
+  return true;
 }
 
 PrefillArgs prefill_args(const moe_shape* s, const moe_layer* L, int rows, const int32_t* offset, const int32_t* perm,
@@ -366,6 +419,11 @@ moe_status moe_layer_decode(const moe_shape* s, const moe_layer* L, const void* 
   if ((st = check_layer(s, L, true, true, true)) != MOE_OK) return st;
   if (!idx || !w || !expert_out || !y) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
+  const bool fused = dt == MOE_BF16
+                         ? launch_decode_fused(s, L, (const uint16_t*)x, off, idx, w, expert_out, y, residual, ws, hs)
+                         : launch_decode_fused(s, L, (const float*)x, off, idx, w, expert_out, y, residual, ws, hs);
+  if (fused) return launched();
+  // the grid does not fit on the device at once: three launches instead
   DecodeArgs A = decode_args(s, L, idx, ws, expert_out, w, y, residual);
   if (dt == MOE_BF16) {
     launch_router(s, L, (const uint16_t*)x, 1, off, idx, w, nullptr, ws, hs);

@@ -92,7 +92,7 @@ __device__ __forceinline__ bool find_mtile(const PrefillArgs& A, bool shared, in
       T.m0 = A.offset[e] + 64 * (mt - t);
       T.mrows = min(64, c - 64 * (mt - t));
       T.F = A.f;
-      T.blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, e);
+      T.blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, e, A.n_experts);
       return T.blob != nullptr;
     }
     t += nt;

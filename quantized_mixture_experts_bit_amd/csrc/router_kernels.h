@@ -18,6 +18,7 @@ __device__ __forceinline__ float x_as_f32(uint16_t v) { return bf16_to_f32(v); }
 
 constexpr int kRouterGPW = 4;                   // groups per wavefront
 constexpr int kRouterGPB = 4 * kRouterGPW;      // groups per workgroup (4 waves)
+constexpr int kMaxRouterSplits = 6;             // d_model <= 6144: at most 96 groups / 16
 
 __device__ __forceinline__ void st_agent_d(double* p, double v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -119,8 +120,13 @@ __global__ __launch_bounds__(256) void k_router(const uint8_t* __restrict__ rout
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
       if (e < n_experts) {
+        double pv[kMaxRouterSplits];  // all loads in flight at once, summed in split order
+#pragma unroll
+        for (int sp = 0; sp < kMaxRouterSplits; ++sp)
+          pv[sp] = sp < nsplit ? ld_agent_d(&partial[((size_t)sp * rows + row) * n_experts + e]) : 0.0;
         double a = 0.0;
-        for (int sp = 0; sp < nsplit; ++sp) a += ld_agent_d(&partial[((size_t)sp * rows + row) * n_experts + e]);
+#pragma unroll
+        for (int sp = 0; sp < kMaxRouterSplits; ++sp) a += pv[sp];
         if (offset) a += (double)offset[e];
         l[j] = a;
         if (logits_out) logits_out[(size_t)row * n_experts + e] = a;
