@@ -69,7 +69,7 @@ DecodeCfg decode_cfg(const moe_shape* s) {
 // different row counts never place a counter where another call kept data.
 struct Ws {
   size_t rt_count, gu_count, dn_count, fused_sync, router_partial, fused_rt, gu_partial, h_hi, h_lo, h_gsum,
-      shared_part, pf_H, pf_Hs, pf_shared_out, pf_xscale, pf_hmax, total;
+      shared_part, pf_H, pf_Hs, pf_shared_out, pf_xscale, pf_hmax, pf_xh, pf_xl, pf_xg, pf_hg, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -99,6 +99,10 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.pf_shared_out = take(sizeof(float) * R * d);
   w.pf_xscale = take(sizeof(float) * R);
   w.pf_hmax = take(sizeof(uint32_t) * R * (k + 1));
+  w.pf_xh = take(sizeof(uint16_t) * R * d);
+  w.pf_xl = take(sizeof(uint16_t) * R * d);
+  w.pf_xg = take(sizeof(float) * R * (d / 64));
+  w.pf_hg = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
   w.total = o;
   return w;
 }
@@ -279,16 +283,31 @@ PrefillArgs prefill_args(const moe_shape* s, const moe_layer* L, int rows, const
   A.shared_out = at<float>(ws, W.pf_shared_out);
   A.xscale = at<float>(ws, W.pf_xscale);
   A.hmax = at<uint32_t>(ws, W.pf_hmax);
+  A.xh = at<uint16_t>(ws, W.pf_xh);
+  A.xl = at<uint16_t>(ws, W.pf_xl);
+  A.xg = at<float>(ws, W.pf_xg);
+  A.hg = at<float>(ws, W.pf_hg);
   return A;
 }
 
+// activation pre-pass, then one gate/up launch and one down launch covering the
+// routed tiles and/or the shared expert's tiles
 template <typename XT>
-void launch_prefill(const PrefillArgs& A, const XT* x, bool routed, bool shared, hipStream_t st) {
-  k_prefill_scales<XT><<<A.rows, 256, 0, st>>>(x, A.rows, A.d, A.top_k, const_cast<float*>(A.xscale), A.hmax);
-  if (routed) k_prefill_gateup<XT><<<A.routed_mtiles * (A.f / 32), 256, 0, st>>>(A, x, 0);
-  if (shared) k_prefill_gateup<XT><<<A.shared_mtiles * (A.fs / 32), 256, 0, st>>>(A, x, 1);
-  if (routed) k_prefill_down<<<A.routed_mtiles * (A.d / 64), 256, 0, st>>>(A, 0);
-  if (shared) k_prefill_down<<<A.shared_mtiles * (A.d / 64), 256, 0, st>>>(A, 1);
+void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, hipStream_t st) {
+  k_prefill_prep<XT><<<A.rows, 256, 0, st>>>(x, A.rows, A.d, A.top_k, A.xscale, A.xh, A.xl, A.xg, A.hmax);
+  if (!routed) A.routed_mtiles = 0;
+  if (!shared) A.shared_mtiles = 0;
+  const int gu_grid = A.routed_mtiles * (A.f / 64) + A.shared_mtiles * (A.fs / 64);
+  const size_t gu_lds = sizeof(float) * 64 * (A.d / 64);
+  if (gu_grid > 0) {
+    if (sizeof(XT) == 4)
+      k_prefill_gateup<true><<<gu_grid, 256, gu_lds, st>>>(A);
+    else
+      k_prefill_gateup<false><<<gu_grid, 256, gu_lds, st>>>(A);
+  }
+  const int dn_grid = (A.routed_mtiles + A.shared_mtiles) * (A.d / 64);
+  const size_t dn_lds = sizeof(float) * 64 * (std::max(A.f, A.fs) / 64);
+  if (dn_grid > 0) k_prefill_down<<<dn_grid, 256, dn_lds, st>>>(A);
 }
 
 }  // namespace
