@@ -69,7 +69,7 @@ DecodeCfg decode_cfg(const moe_shape* s) {
 // different row counts never place a counter where another call kept data.
 struct Ws {
   size_t rt_count, gu_count, dn_count, fused_sync, router_partial, fused_rt, gu_partial, h_hi, h_lo, h_gsum,
-      shared_part, pf_H, pf_Hs, pf_shared_out, pf_xscale, pf_hmax, pf_xh, pf_xl, pf_xg, pf_hg, total;
+      shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -97,12 +97,9 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.pf_H = take(sizeof(float) * R * k * s->d_ff);
   w.pf_Hs = take(sizeof(float) * R * s->d_ff_shared);
   w.pf_shared_out = take(sizeof(float) * R * d);
-  w.pf_xscale = take(sizeof(float) * R);
-  w.pf_hmax = take(sizeof(uint32_t) * R * (k + 1));
-  w.pf_xh = take(sizeof(uint16_t) * R * d);
-  w.pf_xl = take(sizeof(uint16_t) * R * d);
-  w.pf_xg = take(sizeof(float) * R * (d / 64));
-  w.pf_hg = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
+  w.pf_hmaxp = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
+  w.pf_Hh = take(sizeof(uint16_t) * R * ((size_t)k * s->d_ff + s->d_ff_shared));
+  w.pf_hsc = take(sizeof(float) * R * (k + 1));
   w.total = o;
   return w;
 }
@@ -281,33 +278,52 @@ PrefillArgs prefill_args(const moe_shape* s, const moe_layer* L, int rows, const
   A.Hs = at<float>(ws, W.pf_Hs);
   A.expert_out = expert_out;
   A.shared_out = at<float>(ws, W.pf_shared_out);
-  A.xscale = at<float>(ws, W.pf_xscale);
-  A.hmax = at<uint32_t>(ws, W.pf_hmax);
-  A.xh = at<uint16_t>(ws, W.pf_xh);
-  A.xl = at<uint16_t>(ws, W.pf_xl);
-  A.xg = at<float>(ws, W.pf_xg);
-  A.hg = at<float>(ws, W.pf_hg);
+  A.hmaxp = at<float>(ws, W.pf_hmaxp);
+  A.Hh = at<uint16_t>(ws, W.pf_Hh);
+  A.hsc = at<float>(ws, W.pf_hsc);
   return A;
 }
 
-// activation pre-pass, then one gate/up launch and one down launch covering the
-// routed tiles and/or the shared expert's tiles
+// workgroups of `kernel` (256 threads, static LDS only) the device runs at once
+template <typename K>
+int resident_blocks(K kernel, int* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = std::max(1, per_cu * cus);
+  }
+  return cache[dev];
+}
+
+// grid of a persistent GEMM launch: what the chip holds at once (a multiple of the
+// XCD count, so work item i always runs on XCD i % 8), at most the work items
+int persistent_grid(int resident, int items) {
+  int g = std::min(resident, items);
+  if (g > kXcds) g -= g % kXcds;
+  return std::max(g, 1);
+}
+
+// one gate/up launch, the H conversion and one down launch covering the routed
+// tiles and/or the shared expert's tiles
 template <typename XT>
 void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, hipStream_t st) {
-  k_prefill_prep<XT><<<A.rows, 256, 0, st>>>(x, A.rows, A.d, A.top_k, A.xscale, A.xh, A.xl, A.xg, A.hmax);
+  static int cap_gu[64], cap_dn[64];
   if (!routed) A.routed_mtiles = 0;
   if (!shared) A.shared_mtiles = 0;
-  const int gu_grid = A.routed_mtiles * (A.f / 64) + A.shared_mtiles * (A.fs / 64);
-  const size_t gu_lds = sizeof(float) * 64 * (A.d / 64);
-  if (gu_grid > 0) {
-    if (sizeof(XT) == 4)
-      k_prefill_gateup<true><<<gu_grid, 256, gu_lds, st>>>(A);
-    else
-      k_prefill_gateup<false><<<gu_grid, 256, gu_lds, st>>>(A);
-  }
-  const int dn_grid = (A.routed_mtiles + A.shared_mtiles) * (A.d / 64);
-  const size_t dn_lds = sizeof(float) * 64 * (std::max(A.f, A.fs) / 64);
-  if (dn_grid > 0) k_prefill_down<<<dn_grid, 256, dn_lds, st>>>(A);
+  // items at most (routed tile count bounded by the pair count plus one per expert)
+  const int gu_items = xcd_blocks(A.routed_mtiles, A.f / 64) + xcd_blocks(A.shared_mtiles, A.fs / 64);
+  if (gu_items == 0) return;
+  k_prefill_gateup<XT><<<persistent_grid(resident_blocks(k_prefill_gateup<XT>, cap_gu), gu_items), 256, 0, st>>>(A, x);
+  const int P = A.rows * A.top_k;
+  const int first = routed ? 0 : P;
+  const int count = (routed ? P : 0) + (shared ? A.rows : 0);
+  k_prefill_hconv<<<cdiv(count, 4), 256, 0, st>>>(A, first, count);
+  const int dn_items = xcd_blocks(A.routed_mtiles, A.d / 64) + xcd_blocks(A.shared_mtiles, A.d / 64);
+  k_prefill_down<<<persistent_grid(resident_blocks(k_prefill_down, cap_dn), dn_items), 256, 0, st>>>(A);
 }
 
 }  // namespace

@@ -1,26 +1,32 @@
 // Prefill grouped GEMMs on MFMA: each expert's rows (contiguous after grouping)
 // against that expert's weights, one fetch of a weight tile serving every row of
 // the workgroup's row tile.
-//   gate/up: [rows_e x d] x [d x 2*f] on v_mfma_f32_16x16x32_f16, GeGLU in the
+//   gate/up: [rows_e x d] x [d x 2*f] on v_mfma_f32_16x16x32_bf16, GeGLU in the
 //            epilogue, H_e kept in fp32 [rows_e x f];
-//   down:    [rows_e x f] x [f x d], fp32 output per (row, slot) pair.
+//   H pass:  each H row scaled by a power of two and rounded to fp16;
+//   down:    [rows_e x f] x [f x d] on v_mfma_f32_16x16x32_f16, fp32 output per
+//            (row, slot) pair.
 //
 // The 4-bit weights are not dequantised element by element. The affine form is
 // factored out of the contraction per group of 64 columns:
-//   sum_i (s q_i + b) a_i = s * sum_i q_i a_i + b * A_g,
-// where A_g is the group sum of the activations; MFMA computes sum_i q_i a_i per
-// group and the epilogue applies s and b. The B operand is the exact fp16 code q,
-// made from one packed code word (see codes_f16), so the weights enter the
-// product exactly; only the activations are rounded (to fp16, 11 bits):
-// x from bf16 is exact, H from fp32 loses at most 2^-12 relative. Every
-// activation row is scaled by a power of two so its largest magnitude lands in
-// [2^14, 2^15) first (exact), and results are scaled back exactly.
+//   sum_i (s q_i + b) a_i = s * sum_i c_i a_i + (b - s c0) * A_g,   c_i = c0 + q_i,
+// where A_g is the group sum of the activations. MFMA computes sum_i c_i a_i and
+// A_g (a product with a column of ones) per group from the very operands it
+// multiplies; the epilogue applies s and b. Codes and activations enter exactly:
+//   gate/up: x is bf16 (exact; fp32 x is split into two bf16 terms hi + lo),
+//            c_i = 128 + q_i as bf16 from one mask-and-or per code pair (c0 = 128);
+//   down:    H rows scaled so their largest |h| lands in [2^14, 2^15) and rounded
+//            to fp16 (11 bits), c_i = q_i as exact fp16 (c0 = 0), and the
+//            scale divided out at the end (exactly: a power of two).
 //
 // Each wavefront loads its own weight fragments straight from the packed tiles
 // (the tile layout gives lane l the code word of row l%16, columns 8*(l/16)..+7)
-// with kRing groups in flight; activation tiles are staged once per group in
-// double-buffered LDS and shared by the workgroup's four waves.
+// with kRing groups in flight. Activation tiles are fetched several groups ahead
+// into registers, staged once per group in double-buffered LDS and shared by the
+// workgroup's four waves.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -28,9 +34,26 @@ namespace qmoe {
 
 constexpr int kLdsStride = 72;  // halfs per LDS row: 64 + 8 padding (144 B) against bank conflicts
 constexpr int kRing = 4;        // weight groups in flight per wavefront
-constexpr int kMaxGroups = 96;  // d_model or d_ff up to 6144
+constexpr int kXcds = 8;        // accelerator dies, each with its own L2
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// native 128-bit vector (HIP's uint4 is a struct: copies of it through register
+// arrays become private-memory copies that stay in scratch)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, i>) for i = 0..N-1: ring slots must be compile-time
+// indices, or the register arrays that hold them are demoted to scratch memory
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int I>
+using ic = std::integral_constant<int, I>;
 
 struct PrefillArgs {
   const uint8_t* pool;
@@ -42,14 +65,11 @@ struct PrefillArgs {
   int d, f, fs, n_experts, top_k, rows;
   int routed_mtiles;      // upper bound of routed 64-row tiles
   int shared_mtiles;      // 64-row tiles of the shared expert
-  float* xscale;          // [rows] power-of-two activation scale per row
-  uint16_t* xh;           // [rows][d] fp16 of x * scale
-  uint16_t* xl;           // [rows][d] fp16 remainder (fp32 x only)
-  float* xg;              // [rows][d/64] group sums of the scaled fp16 activations (hi + lo)
   float* H;               // routed GeGLU output, fp32 [rows*top_k][f] (sorted-pair order)
   float* Hs;              // shared GeGLU output, fp32 [rows][fs]
-  float* hg;              // routed H group sums [rows*top_k][f/64], then shared [rows][fs/64]
-  uint32_t* hmax;         // [rows*top_k] max |H| per routed row (float bits), then [rows] shared
+  float* hmaxp;           // max |h| per (row, 64-column block): routed [rows*top_k][f/64], then shared [rows][fs/64]
+  uint16_t* Hh;           // fp16 of h * hsc: routed [rows*top_k][f], then shared [rows][fs]
+  float* hsc;             // power-of-two row scale of Hh: routed [rows*top_k], then shared [rows]
   float* expert_out;      // [rows*top_k][d]
   float* shared_out;      // [rows][d]
 };
@@ -61,52 +81,95 @@ struct MTile {
   int F;
 };
 
-// Routed tiles are numbered expert by expert (ceil(count_e / 64) tiles each).
-// The wavefront finds tile `mt` with a prefix sum over the per-expert tile counts
-// (lane l covers experts [l*epl, (l+1)*epl)). Every lane returns the same tile.
-__device__ __forceinline__ bool find_mtile(const PrefillArgs& A, bool shared, int mt, MTile& T) {
-  if (shared) {
-    if (mt >= A.shared_mtiles) return false;
-    T.e = -1;
-    T.m0 = 64 * mt;
-    T.mrows = min(64, A.rows - T.m0);
-    T.blob = A.shared_blob;
-    T.F = A.fs;
-    return true;
-  }
-  if (mt >= A.routed_mtiles) return false;
+// Routed tiles are numbered expert by expert (ceil(count_e / 64) tiles each). Each
+// lane of a wavefront keeps the ranges of experts [l*epl, (l+1)*epl) (epl <= 4)
+// and the prefix of their tile counts, so a tile is found with one ballot.
+struct TileMap {
+  int excl, incl;  // tiles of the experts before this lane's, and including them
+  int off[4], cnt[4];
+};
+
+// Fills the map from the grouping offsets; returns the number of routed tiles.
+__device__ __forceinline__ int tile_map_init(const PrefillArgs& A, TileMap& M) {
   const int lane = threadIdx.x & 63;
   const int epl = A.n_experts / 64;
   int mine = 0;
-  for (int j = 0; j < epl; ++j) {
-    const int e = lane * epl + j;
-    mine += (A.offset[e + 1] - A.offset[e] + 63) >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    M.off[j] = M.cnt[j] = 0;
+    if (j < epl) {
+      const int e = lane * epl + j;
+      M.off[j] = A.offset[e];
+      M.cnt[j] = A.offset[e + 1] - M.off[j];
+      mine += (M.cnt[j] + 63) >> 6;
+    }
   }
   int incl = mine;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
-  const int excl = incl - mine;
-  const uint64_t hit = __ballot(mt >= excl && mt < incl);
+  M.excl = incl - mine;
+  M.incl = incl;
+  return __shfl(incl, 63, 64);
+}
+
+// 64-row tile -> (expert, first sorted position, row count, weights); every lane
+// returns the same tile. False for an expert with no resident weights.
+__device__ __forceinline__ bool tile_at(const PrefillArgs& A, const TileMap& M, int mt, MTile& T) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t hit = __ballot(mt >= M.excl && mt < M.incl);
   if (hit == 0) return false;
   const int owner = __ffsll((unsigned long long)hit) - 1;
-  int t = __shfl(excl, owner, 64);
-  int e = owner * epl;
-  for (;; ++e) {
-    const int c = A.offset[e + 1] - A.offset[e];
-    const int nt = (c + 63) >> 6;
-    if (mt < t + nt) {
-      T.e = e;
-      T.m0 = A.offset[e] + 64 * (mt - t);
-      T.mrows = min(64, c - 64 * (mt - t));
-      T.F = A.f;
-      T.blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, e, A.n_experts);
-      return T.blob != nullptr;
+  int e = 0, m0 = 0, mr = 0;
+  if (lane == owner) {
+    const int epl = A.n_experts / 64;
+    int t = M.excl;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nt = (M.cnt[j] + 63) >> 6;
+      if (j < epl && !found && mt < t + nt) {
+        found = true;
+        e = lane * epl + j;
+        m0 = M.off[j] + 64 * (mt - t);
+        mr = min(64, M.cnt[j] - 64 * (mt - t));
+      }
+      t += nt;
     }
-    t += nt;
   }
+  T.e = __shfl(e, owner, 64);
+  T.m0 = __shfl(m0, owner, 64);
+  T.mrows = __shfl(mr, owner, 64);
+  T.F = A.f;
+  T.blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, T.e, A.n_experts);
+  return T.blob != nullptr;
+}
+
+__device__ __forceinline__ void shared_tile(const PrefillArgs& A, int mt, MTile& T) {
+  T.e = -1;
+  T.m0 = 64 * mt;
+  T.mrows = min(64, A.rows - T.m0);
+  T.blob = A.shared_blob;
+  T.F = A.fs;
+}
+
+// Workgroups are dealt to the XCDs round robin by block index. A section of `nt`
+// row tiles x `nc` column blocks is laid out so that all column blocks of one row
+// tile land on the same XCD (its activation tile is fetched into that L2 once)
+// and consecutive row tiles go to different XCDs. `lanes` = min(kXcds, nt).
+__host__ __device__ inline int xcd_lanes(int nt) { return nt < kXcds ? (nt > 0 ? nt : 1) : kXcds; }
+__host__ __device__ inline int xcd_blocks(int nt, int nc) {
+  const int k = xcd_lanes(nt);
+  return (nt + k - 1) / k * k * nc;
+}
+__device__ __forceinline__ void xcd_item(int b, int nt, int nc, int& mt, int& c) {
+  const int k = xcd_lanes(nt);
+  const int per = k * nc;
+  const int q = b / per, r = b - q * per;
+  mt = q * k + r % k;
+  c = r / k;
 }
 
 // power of two that brings a row maximum m (> 0) into [2^14, 2^15); 1 for m == 0
@@ -116,15 +179,16 @@ __device__ __forceinline__ float row_scale(float m) {
   return ldexpf(1.0f, min(14 - e, 126));
 }
 
-__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
-__device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ uint16_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
-__device__ __forceinline__ float f16_val(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// B operand, gate/up: the 8 codes of one packed word as bf16 (128 + q)
+__device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w) {
+  const u32x4_t p = {nib_pair(w, 0), nib_pair(w, 1), nib_pair(w, 2), nib_pair(w, 3)};
+  return __builtin_bit_cast(bf16x8_t, p);
+}
 
-// B operand: the 8 codes of one packed word as exact fp16 values q (0..15): the
-// pair (1024 + q, 1024 + q') is built with a mask and an OR of the exponent of
+// B operand, down: the 8 codes of one packed word as exact fp16 values q (0..15):
+// the pair (1024 + q, 1024 + q') is built with a mask and an OR of the exponent of
 // 1024 (0x6400), then 1024 is subtracted with one packed fp16 add per pair.
 __device__ __forceinline__ f16x8_t codes_f16(uint32_t w) {
   const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
@@ -135,71 +199,27 @@ __device__ __forceinline__ f16x8_t codes_f16(uint32_t w) {
   return f16x8_t{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
-__device__ __forceinline__ f16x8_t lds_frag(const uint16_t* p) {
-  return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(p));
+template <typename V>
+__device__ __forceinline__ V lds_frag(const uint16_t* p) {
+  return __builtin_bit_cast(V, *reinterpret_cast<const u32x4_t*>(p));
 }
 
-// ---------------------------------------------------------------- activation pre-pass
-
-// One workgroup per activation row: power-of-two scale, fp16 copy (x * scale, plus
-// the fp16 rounding remainder for fp32 x), group sums of the fp16 values, and the
-// clearing of the row's H maxima (its routed pairs, then its shared-expert row).
-template <typename XT>
-__global__ __launch_bounds__(256) void k_prefill_prep(const XT* __restrict__ x, int rows, int d, int top_k,
-                                                      float* __restrict__ xscale, uint16_t* __restrict__ xh,
-                                                      uint16_t* __restrict__ xl, float* __restrict__ xg,
-                                                      uint32_t* __restrict__ hmax) {
-  constexpr bool kLo = sizeof(XT) == 4;
-  __shared__ float red[4];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const XT* xr = x + (size_t)r * d;
-  float m = 0.0f;
-  for (int i = tid; i < d; i += 256) m = fmaxf(m, fabsf(to_f32(xr[i])));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  const float sc = row_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-  if (tid == 0) xscale[r] = sc;
-  if (tid < top_k) hmax[r * top_k + tid] = 0u;
-  if (tid == 0) hmax[rows * top_k + r] = 0u;
-  const int G = d / kGroup;
-  for (int g = wave; g < G; g += 4) {
-    const int i = g * kGroup + lane;
-    const float v = to_f32(xr[i]) * sc;
-    const uint16_t hb = f16_bits(v);
-    float s = f16_val(hb);
-    xh[(size_t)r * d + i] = hb;
-    if (kLo) {
-      const uint16_t lb = f16_bits(v - f16_val(hb));
-      xl[(size_t)r * d + i] = lb;
-      s += f16_val(lb);
-    }
-    s = wave_sum(s);
-    if (lane == 0) xg[(size_t)r * G + g] = s;
-  }
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- shared GEMM core
-
-// Accumulates a [64-row tile] x [one 16-column n-block per matrix, NM matrices] product
-// over K groups: acc[mb][m] += s * sum q a + b * a_g, per group.
-// A (activations, fp16, row-scaled) arrives through LDS; `stage(g, buf)` must fill
-// LDS buffer `buf` with group g. B comes from the packed tiles at wbase[m] +
-// g * kTile4 (+ kh*1024 + row*16 + (lane/16)*4), scales at + 2048 + row*4.
-template <int NM, bool LO>
-struct GemmCore {
-  f32x4_t acc[4][NM];
+// Weight fragments of NM matrices in a ring of kRing groups: for wave row `row`
+// (0..63 within the 64-row block), the two code words of k-halves 0 and 1 and the
+// (scale, bias) pair, from tile g at wbase[m] + g * kTile4.
+template <int NM>
+struct BRing {
   uint32_t cw[kRing][NM][2];
   uint32_t sb[kRing][NM];
-
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) acc[i][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  __device__ __forceinline__ void load_b(int slot, const uint8_t* const* wbase, int g, int row, int lane) {
+  template <int slot>
+  __device__ __forceinline__ void load(ic<slot>, const uint8_t* const* wbase, int g, int row, int lane) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const uint8_t* t = wbase[m] + (uint64_t)g * kTile4;
@@ -210,148 +230,176 @@ struct GemmCore {
   }
 };
 
+__device__ __forceinline__ void zero_acc(f32x4_t& a) { a = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+
 // ---------------------------------------------------------------- gate/up + GeGLU
 
-// Workgroup = (64-row tile, 64 d_ff columns). Wave w owns d_ff columns [16w, +16) of
-// both gate and up (so GeGLU runs in registers) for every row of the tile.
-// Routed tiles first: blockIdx < routed_mtiles * f/64, then shared tiles.
+// LDS of the gate/up kernel: double-buffered activation tiles (bf16 hi, and lo for
+// fp32 x) and the per-wave row maxima of |h|
 template <bool LO>
-__global__ __launch_bounds__(256) void k_prefill_gateup(PrefillArgs A) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][64 * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Xls[LO ? 2 : 1][LO ? 64 * kLdsStride : 8];
-  extern __shared__ float4 dyn_lds[];  // [G][64] activation group sums
-  float(*XgL)[64] = reinterpret_cast<float(*)[64]>(dyn_lds);
-  __shared__ int rowsrc[64];
-  __shared__ float rowinv[64];
-  __shared__ float hsumL[4][64];
+struct GateupSmem {
+  __attribute__((aligned(16))) uint16_t Xs[2][64 * kLdsStride];
+  __attribute__((aligned(16))) uint16_t Xls[LO ? 2 : 1][LO ? 64 * kLdsStride : 8];
+  float hmL[4][64];
+};
 
-  const int nfr = A.f / 64;
-  int b = blockIdx.x;
-  bool shared = false;
-  int nfc = nfr;
-  if (b >= A.routed_mtiles * nfr) {
-    b -= A.routed_mtiles * nfr;
-    shared = true;
-    nfc = A.fs / 64;
-  }
-  const int mt = b / nfc, fc = b % nfc;
-  MTile T;
-  if (!find_mtile(A, shared, mt, T)) return;
+// One work item = (64-row tile, 64 d_ff columns). Wave w owns d_ff columns [16w, +16)
+// of both gate and up (so GeGLU runs in registers) for every row of the tile.
+template <typename XT>
+__device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __restrict__ x, const MTile& T, int fc,
+                                            bool shared, GateupSmem<sizeof(XT) == 4>& S) {
+  constexpr bool LO = sizeof(XT) == 4;  // fp32 x: hi + lo bf16 terms
+  constexpr int RA = LO ? 2 : 4;        // activation groups in flight
+  constexpr int NV = LO ? 4 : 2;        // 16-byte loads per thread per group
+  auto& Xs = S.Xs;
+  auto& Xls = S.Xls;
+  auto& hmL = S.hmL;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = A.d / kGroup;
   const int nmb = (T.mrows + 15) >> 4;
 
-  if (tid < 64) {
-    int src = -1;
-    if (tid < T.mrows) src = (T.e >= 0) ? A.perm[T.m0 + tid] / A.top_k : T.m0 + tid;
-    rowsrc[tid] = src;
-    rowinv[tid] = src >= 0 ? 1.0f / A.xscale[src] : 1.0f;  // exact: a power of two
-  }
-  __syncthreads();
-  for (int i = tid; i < 64 * G; i += 256) {
-    const int r = i / G, g = i % G;
-    const int src = rowsrc[r];
-    XgL[g][r] = src >= 0 ? A.xg[(size_t)src * G + g] : 0.0f;
-  }
-
-  // this wave's weight rows: row 16*wave + lane%16 of the 64-row block fc of gate and up
+  // weight rows of this wave: row 16*wave + lane%16 of the 64-row block fc of gate and up
   const int wrow = 16 * wave + (lane & 15);
   const uint8_t* wbase[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
     wbase[m] = T.blob + (uint64_t)m * m4_bytes(T.F, A.d) + (uint64_t)fc * G * kTile4;
-  GemmCore<2, LO> C;
-  C.zero();
-#pragma unroll
-  for (int j = 0; j < kRing; ++j)
-    if (j < G) C.load_b(j, wbase, j, wrow, lane);
+  BRing<2> B;
 
-  // activation staging: thread -> row tid/4, 16 halfs at column (tid%4)*16
+  // activation staging: thread -> tile row tid/4, 16 values at column (tid%4)*16.
+  // Rows past the tile's end repeat its first row: MFMA output rows depend on their
+  // own A rows only, and those rows are never stored, so the loads need no branch.
   const int xr = tid >> 2, xq = tid & 3;
-  const int xsrc = rowsrc[xr];
-  const uint16_t* xrow = A.xh + (size_t)(xsrc >= 0 ? xsrc : 0) * A.d + xq * 16;
-  const uint16_t* xrowl = LO ? A.xl + (size_t)(xsrc >= 0 ? xsrc : 0) * A.d + xq * 16 : nullptr;
-  uint4 xa[2], xla[2];
-  auto xload = [&](int g) {
-    if (xsrc >= 0) {
-      xa[0] = *reinterpret_cast<const uint4*>(xrow + g * kGroup);
-      xa[1] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + 8);
-      if (LO) {
-        xla[0] = *reinterpret_cast<const uint4*>(xrowl + g * kGroup);
-        xla[1] = *reinterpret_cast<const uint4*>(xrowl + g * kGroup + 8);
-      }
+  const int xt = xr < T.mrows ? xr : 0;
+  const int xsrc = T.e >= 0 ? A.perm[T.m0 + xt] / A.top_k : T.m0 + xt;
+  const XT* xrow = x + (size_t)xsrc * A.d + xq * 16;
+  u32x4_t xa[RA][NV];
+  auto aload = [&](auto sc, int g) __attribute__((always_inline)) {
+    constexpr int slot = decltype(sc)::value;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      xa[slot][v] = *reinterpret_cast<const u32x4_t*>(xrow + g * kGroup + v * (16 / sizeof(XT)));
+  };
+  auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
+    constexpr int slot = decltype(sc)::value;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&Xs[buf][xr * kLdsStride + xq * 16]);
+    if (!LO) {
+      dst[0] = xa[slot][0];
+      dst[1] = xa[slot][1];
     } else {
-      xa[0] = xa[1] = xla[0] = xla[1] = make_uint4(0, 0, 0, 0);
+      // 16 fp32 values -> bf16 hi (round to nearest even) and bf16 lo of the remainder
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t w[4] = {xa[slot][v].x, xa[slot][v].y, xa[slot][v].z, xa[slot][v].w};
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          uint32_t h2 = 0, l2 = 0;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float f = __uint_as_float(w[2 * p + q]);
+            const uint32_t hb = f32_to_bf16_bits(f);
+            const uint32_t lb = f32_to_bf16_bits(f - __uint_as_float(hb << 16));
+            h2 |= hb << (16 * q);
+            l2 |= lb << (16 * q);
+          }
+          hi[2 * v + p] = h2;
+          lo[2 * v + p] = l2;
+        }
+      }
+      u32x4_t* dl = reinterpret_cast<u32x4_t*>(&Xls[buf][xr * kLdsStride + xq * 16]);
+      dst[0] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+      dst[1] = u32x4_t{hi[4], hi[5], hi[6], hi[7]};
+      dl[0] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+      dl[1] = u32x4_t{lo[4], lo[5], lo[6], lo[7]};
     }
   };
-  auto xstore = [&](int buf) {
-    uint4* d = reinterpret_cast<uint4*>(&Xs[buf][xr * kLdsStride + xq * 16]);
-    d[0] = xa[0];
-    d[1] = xa[1];
-    if (LO) {
-      uint4* dl = reinterpret_cast<uint4*>(&Xls[buf][xr * kLdsStride + xq * 16]);
-      dl[0] = xla[0];
-      dl[1] = xla[1];
+  // prologue: the loads in the order the steady state issues them (weights of group
+  // j, then activations of group j + 1), so the wait counts agree on entry
+  aload(ic<0>{}, 0);
+  static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    B.load(jc, wbase, min(j, G - 1), wrow, lane);
+    if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(j + 1, G - 1));
+    if constexpr (j + 1 == RA) {
+      astore(ic<0>{}, 0);
+      aload(ic<0>{}, min(RA, G - 1));
     }
-  };
-  xload(0);
-  xstore(0);
-  if (G > 1) xload(1);
+  });
   __syncthreads();
 
-  for (int g0 = 0; g0 < G; g0 += kRing) {
+  f32x4_t acc[4][2];
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-      const int g = g0 + j;
-      if (g < G) {
-        const int buf = g & 1;
-        // B fragments and scales of this group, then refill the ring slot
-        f16x8_t bfr[2][2];
-        float s[2], bp[2];
+  for (int mb = 0; mb < 4; ++mb) {
+    zero_acc(acc[mb][0]);
+    zero_acc(acc[mb][1]);
+  }
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  // One K group: MFMAs from LDS buffer j&1 and weight slot j; then the weight
+  // slot is refilled with group g + kRing and the activation slot staged next is
+  // refilled with group g + 1 + RA, both clamped to the last group (the surplus
+  // loads near the end are never used). The steady-state loop is
+  // straight-line code over kRing groups, so every ring slot keeps its own
+  // registers and no wait covers a load younger than the one it needs.
+  auto step = [&](auto jc, int g) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int buf = j & 1;
+    bf16x8_t bfr[2][2];
+    float s[2], bb[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          bfr[m][0] = codes_f16(C.cw[j][m][0]);
-          bfr[m][1] = codes_f16(C.cw[j][m][1]);
-          s[m] = bf16_lo(C.sb[j][m]);
-          bp[m] = bf16_hi(C.sb[j][m]);
+    for (int m = 0; m < 2; ++m) {
+      bfr[m][0] = codes_bf16(B.cw[j][m][0]);
+      bfr[m][1] = codes_bf16(B.cw[j][m][1]);
+      s[m] = bf16_lo(B.sb[j][m]);
+      bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
+    }
+    B.load(jc, wbase, min(g + kRing, G - 1), wrow, lane);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb < nmb) {
+        const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
+        const bf16x8_t a0 = lds_frag<bf16x8_t>(&Xs[buf][ao]);
+        const bf16x8_t a1 = lds_frag<bf16x8_t>(&Xs[buf][ao + 32]);
+        f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        f32x4_t t[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) t[m] = mfma(a1, bfr[m][1], mfma(a0, bfr[m][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        if (LO) {
+          const bf16x8_t l0 = lds_frag<bf16x8_t>(&Xls[buf][ao]);
+          const bf16x8_t l1 = lds_frag<bf16x8_t>(&Xls[buf][ao + 32]);
+          ag = mfma(l1, ones, mfma(l0, ones, ag));
+#pragma unroll
+          for (int m = 0; m < 2; ++m) t[m] = mfma(l1, bfr[m][1], mfma(l0, bfr[m][0], t[m]));
         }
-        if (g + kRing < G) C.load_b(j, wbase, g + kRing, wrow, lane);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if (mb < nmb) {
-            const int arow = 16 * mb + (lane & 15);
-            const f16x8_t a0 = lds_frag(&Xs[buf][arow * kLdsStride + 8 * (lane >> 4)]);
-            const f16x8_t a1 = lds_frag(&Xs[buf][arow * kLdsStride + 32 + 8 * (lane >> 4)]);
-            const float4 xg4 = *reinterpret_cast<const float4*>(&XgL[g][16 * mb + 4 * (lane >> 4)]);
-            const float xgv[4] = {xg4.x, xg4.y, xg4.z, xg4.w};
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bfr[m][0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-              t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bfr[m][1], t, 0, 0, 0);
-              if (LO) {
-                const f16x8_t l0 = lds_frag(&Xls[buf][arow * kLdsStride + 8 * (lane >> 4)]);
-                const f16x8_t l1 = lds_frag(&Xls[buf][arow * kLdsStride + 32 + 8 * (lane >> 4)]);
-                t = __builtin_amdgcn_mfma_f32_16x16x32_f16(l0, bfr[m][0], t, 0, 0, 0);
-                t = __builtin_amdgcn_mfma_f32_16x16x32_f16(l1, bfr[m][1], t, 0, 0, 0);
-              }
-#pragma unroll
-              for (int i = 0; i < 4; ++i) C.acc[mb][m][i] = fmaf(s[m], t[i], fmaf(bp[m], xgv[i], C.acc[mb][m][i]));
-            }
-          }
-        }
-        // next activation group into the other buffer (its readers passed the last barrier)
-        if (g + 1 < G) xstore(buf ^ 1);
-        if (g + 2 < G) xload(g + 2);
-        __syncthreads();
+          for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[m][i], fmaf(bb[m], ag[i], acc[mb][m][i]));
       }
     }
+    // next activation group into the other buffer (its readers passed the last barrier)
+    astore(ic<(j + 1) % RA>{}, buf ^ 1);
+    aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, G - 1));
+    __syncthreads();
+  };
+  int g0 = 0;
+  for (; g0 + kRing <= G; g0 += kRing) {
+    step(ic<0>{}, g0);
+    step(ic<1>{}, g0 + 1);
+    step(ic<2>{}, g0 + 2);
+    step(ic<3>{}, g0 + 3);
   }
+  // the last G % kRing groups
+  if (g0 < G) step(ic<0>{}, g0);
+  if (g0 + 1 < G) step(ic<1>{}, g0 + 1);
+  if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
 
   // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16
-  float* H = (T.e >= 0) ? A.H : A.Hs;
-  float* hg = (T.e >= 0) ? A.hg : A.hg + (size_t)A.rows * A.top_k * (A.f / 64);
-  uint32_t* hmax = (T.e >= 0) ? A.hmax : A.hmax + (size_t)A.rows * A.top_k;
+  float* H = shared ? A.Hs : A.H;
+  float* hmaxp = shared ? A.hmaxp + (size_t)A.rows * A.top_k * (A.f / 64) : A.hmaxp;
   const int F = T.F, nG = F / 64;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -360,134 +408,217 @@ __global__ __launch_bounds__(256) void k_prefill_gateup(PrefillArgs A) {
       const int r = 16 * mb + 4 * (lane >> 4) + i;
       float h = 0.0f;
       if (r < T.mrows) {
-        const float inv = rowinv[r];
-        h = gelu_tanh(C.acc[mb][0][i] * inv) * (C.acc[mb][1][i] * inv);
+        h = gelu_tanh(acc[mb][0][i]) * acc[mb][1][i];
         H[(size_t)(T.m0 + r) * F + fc * 64 + 16 * wave + (lane & 15)] = h;
       }
-      // over the 16 lanes holding this row: max |h| (row scale of the down GEMM) and sum
-      float mx = fabsf(h), sm = h;
+      // max |h| over the 16 lanes holding this row
+      float mx = fabsf(h);
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        sm += __shfl_xor(sm, off, 64);
-      }
-      if ((lane & 15) == 0 && r < 64) {
-        if (r < T.mrows) atomicMax(&hmax[T.m0 + r], __float_as_uint(mx));
-        hsumL[wave][r] = sm;
-      }
+      for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      if ((lane & 15) == 0) hmL[wave][r] = mx;
     }
   __syncthreads();
   if (tid < T.mrows)
-    hg[(size_t)(T.m0 + tid) * nG + fc] = ((hsumL[0][tid] + hsumL[1][tid]) + hsumL[2][tid]) + hsumL[3][tid];
+    hmaxp[(size_t)(T.m0 + tid) * nG + fc] = fmaxf(fmaxf(hmL[0][tid], hmL[1][tid]), fmaxf(hmL[2][tid], hmL[3][tid]));
+}
+
+// Persistent: a grid sized to what the chip holds at once walks the work items
+// (shared-expert items first: they are the longest; then the routed tiles that
+// exist), so no workgroup slot goes to an empty tile.
+template <typename XT>
+__global__ __launch_bounds__(256, 2) void k_prefill_gateup(PrefillArgs A, const XT* __restrict__ x) {
+  __shared__ GateupSmem<sizeof(XT) == 4> S;
+  TileMap M;
+  const int nrt = A.routed_mtiles > 0 ? tile_map_init(A, M) : 0;
+  const int ncs = A.fs / 64, ncr = A.f / 64;
+  const int ns = xcd_blocks(A.shared_mtiles, ncs);
+  const int n = ns + xcd_blocks(nrt, ncr);
+  for (int item = blockIdx.x; item < n; item += gridDim.x) {
+    const bool shared = item < ns;
+    int mt, fc;
+    MTile T;
+    if (shared) {
+      xcd_item(item, A.shared_mtiles, ncs, mt, fc);
+      if (mt >= A.shared_mtiles) continue;
+      shared_tile(A, mt, T);
+    } else {
+      xcd_item(item - ns, nrt, ncr, mt, fc);
+      if (mt >= nrt || !tile_at(A, M, mt, T)) continue;
+    }
+    gateup_tile<XT>(A, x, T, fc, shared, S);
+    __syncthreads();  // the next item reuses the LDS
+  }
+}
+
+// ---------------------------------------------------------------- H to fp16
+
+// One wavefront per H row (rows [first, first + count) of the routed rows followed
+// by the shared rows): the row's power-of-two scale from its per-block maxima,
+// then the fp16 copy of h * scale.
+__global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first, int count) {
+  const int lane = threadIdx.x & 63;
+  const int r = first + (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (r >= first + count) return;
+  const int P = A.rows * A.top_k;
+  const float* src;
+  const float* mp;
+  uint16_t* dst;
+  int F;
+  if (r < P) {
+    F = A.f;
+    src = A.H + (size_t)r * F;
+    mp = A.hmaxp + (size_t)r * (F / 64);
+    dst = A.Hh + (size_t)r * F;
+  } else {
+    const int rs = r - P;
+    F = A.fs;
+    src = A.Hs + (size_t)rs * F;
+    mp = A.hmaxp + (size_t)P * (A.f / 64) + (size_t)rs * (F / 64);
+    dst = A.Hh + (size_t)P * A.f + (size_t)rs * F;
+  }
+  float m = 0.0f;
+  for (int i = lane; i < F / 64; i += 64) m = fmaxf(m, mp[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float sc = row_scale(m);
+  if (lane == 0) A.hsc[r] = sc;
+  for (int c = 4 * lane; c < F; c += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(src + c);
+    const uint32_t p0 = (uint32_t)f16_bits(v.x * sc) | ((uint32_t)f16_bits(v.y * sc) << 16);
+    const uint32_t p1 = (uint32_t)f16_bits(v.z * sc) | ((uint32_t)f16_bits(v.w * sc) << 16);
+    *reinterpret_cast<uint2*>(dst + c) = make_uint2(p0, p1);
+  }
 }
 
 // ---------------------------------------------------------------- down
 
-// Workgroup = (64-row tile, 64 output columns). Wave w owns output columns [16w, +16)
-// for every row of the tile. Routed tiles first, then shared.
-__global__ __launch_bounds__(256) void k_prefill_down(PrefillArgs A) {
-  __shared__ __attribute__((aligned(16))) uint16_t Hl[2][64 * kLdsStride];
-  __shared__ float rowsc[64];
-  extern __shared__ float4 dyn_lds[];  // [G][64] H group sums (scaled)
-  float(*hgL)[64] = reinterpret_cast<float(*)[64]>(dyn_lds);
-  const int NBd = A.d / 64;
-  int b = blockIdx.x;
-  bool shared = false;
-  if (b >= A.routed_mtiles * NBd) {
-    b -= A.routed_mtiles * NBd;
-    shared = true;
-  }
-  const int mt = b / NBd, nb = b % NBd;
-  MTile T;
-  if (!find_mtile(A, shared, mt, T)) return;
+struct DownSmem {
+  __attribute__((aligned(16))) uint16_t Hl[2][64 * kLdsStride];
+  float rowinv[64];
+};
+
+// One work item = (64-row tile, 64 output columns). Wave w owns output columns
+// [16w, +16) for every row of the tile.
+__device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, int nb, bool shared, DownSmem& S) {
+  constexpr int RA = 4;
+  auto& Hl = S.Hl;
+  auto& rowinv = S.rowinv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int F = T.F, G = F / kGroup;
   const int nmb = (T.mrows + 15) >> 4;
-  const float* Hsrc = (T.e >= 0) ? A.H : A.Hs;
-  const float* hg = (T.e >= 0) ? A.hg : A.hg + (size_t)A.rows * A.top_k * (A.f / 64);
-  const uint32_t* hmax = (T.e >= 0) ? A.hmax : A.hmax + (size_t)A.rows * A.top_k;
-  if (tid < 64) rowsc[tid] = tid < T.mrows ? row_scale(__uint_as_float(hmax[T.m0 + tid])) : 1.0f;
-  __syncthreads();
-  for (int i = tid; i < 64 * G; i += 256) {
-    const int r = i / G, g = i % G;
-    hgL[g][r] = r < T.mrows ? hg[(size_t)(T.m0 + r) * G + g] * rowsc[r] : 0.0f;
-  }
+  const int P = A.rows * A.top_k;
+  const uint16_t* Hh = shared ? A.Hh + (size_t)P * A.f : A.Hh;
+  const float* hsc = shared ? A.hsc + P : A.hsc;
 
   const int wrow = 16 * wave + (lane & 15);
   const uint8_t* wbase[1] = {T.blob + 2 * m4_bytes(F, A.d) + (uint64_t)nb * G * kTile4};
-  GemmCore<1, false> C;
-  C.zero();
-#pragma unroll
-  for (int j = 0; j < kRing; ++j)
-    if (j < G) C.load_b(j, wbase, j, wrow, lane);
+  BRing<1> B;
+  if (tid < 64) rowinv[tid] = tid < T.mrows ? 1.0f / hsc[T.m0 + tid] : 1.0f;  // exact: powers of two
 
-  // H staging: thread -> row tid/4, 16 values at column (tid%4)*16, scaled to fp16
+  // H staging: thread -> tile row tid/4, 16 halfs at column (tid%4)*16; rows past
+  // the tile's end repeat its first row (see the gate/up kernel)
   const int hr = tid >> 2, hq = tid & 3;
-  const bool hvalid = hr < T.mrows;
-  const float hsc = rowsc[hr];
-  const float* hrow = Hsrc + (size_t)(T.m0 + (hvalid ? hr : 0)) * F + hq * 16;
-  float4 hv[4];
-  auto hload = [&](int g) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      hv[i] = hvalid ? *reinterpret_cast<const float4*>(hrow + g * kGroup + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const uint16_t* hrow = Hh + (size_t)(T.m0 + (hr < T.mrows ? hr : 0)) * F + hq * 16;
+  u32x4_t ha[RA][2];
+  auto aload = [&](auto sc, int g) __attribute__((always_inline)) {
+    constexpr int slot = decltype(sc)::value;
+    ha[slot][0] = *reinterpret_cast<const u32x4_t*>(hrow + g * kGroup);
+    ha[slot][1] = *reinterpret_cast<const u32x4_t*>(hrow + g * kGroup + 8);
   };
-  auto hstore = [&](int buf) {
-    uint32_t p[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[2 * i] = (uint32_t)f16_bits(hv[i].x * hsc) | ((uint32_t)f16_bits(hv[i].y * hsc) << 16);
-      p[2 * i + 1] = (uint32_t)f16_bits(hv[i].z * hsc) | ((uint32_t)f16_bits(hv[i].w * hsc) << 16);
+  auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
+    constexpr int slot = decltype(sc)::value;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&Hl[buf][hr * kLdsStride + hq * 16]);
+    dst[0] = ha[slot][0];
+    dst[1] = ha[slot][1];
+  };
+  // prologue: the loads in the order the steady state issues them (weights of group
+  // j, then activations of group j + 1), so the wait counts agree on entry
+  aload(ic<0>{}, 0);
+  static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    B.load(jc, wbase, min(j, G - 1), wrow, lane);
+    if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(j + 1, G - 1));
+    if constexpr (j + 1 == RA) {
+      astore(ic<0>{}, 0);
+      aload(ic<0>{}, min(RA, G - 1));
     }
-    uint4* d = reinterpret_cast<uint4*>(&Hl[buf][hr * kLdsStride + hq * 16]);
-    d[0] = make_uint4(p[0], p[1], p[2], p[3]);
-    d[1] = make_uint4(p[4], p[5], p[6], p[7]);
-  };
-  hload(0);
-  hstore(0);
-  if (G > 1) hload(1);
+  });
   __syncthreads();
 
-  for (int g0 = 0; g0 < G; g0 += kRing) {
+  f32x4_t acc[4];
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-      const int g = g0 + j;
-      if (g < G) {
-        const int buf = g & 1;
-        const f16x8_t b0 = codes_f16(C.cw[j][0][0]);
-        const f16x8_t b1 = codes_f16(C.cw[j][0][1]);
-        const float s = bf16_lo(C.sb[j][0]);
-        const float bp = bf16_hi(C.sb[j][0]);
-        if (g + kRing < G) C.load_b(j, wbase, g + kRing, wrow, lane);
+  for (int mb = 0; mb < 4; ++mb) zero_acc(acc[mb]);
+  const f16x8_t ones = __builtin_bit_cast(f16x8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+
+  // one K group, as in the gate/up kernel
+  auto step = [&](auto jc, int g) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int buf = j & 1;
+    const f16x8_t b0 = codes_f16(B.cw[j][0][0]);
+    const f16x8_t b1 = codes_f16(B.cw[j][0][1]);
+    const float s = bf16_lo(B.sb[j][0]);
+    const float bp = bf16_hi(B.sb[j][0]);
+    B.load(jc, wbase, min(g + kRing, G - 1), wrow, lane);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if (mb < nmb) {
-            const int arow = 16 * mb + (lane & 15);
-            const f16x8_t a0 = lds_frag(&Hl[buf][arow * kLdsStride + 8 * (lane >> 4)]);
-            const f16x8_t a1 = lds_frag(&Hl[buf][arow * kLdsStride + 32 + 8 * (lane >> 4)]);
-            const float4 hg4 = *reinterpret_cast<const float4*>(&hgL[g][16 * mb + 4 * (lane >> 4)]);
-            const float hgv[4] = {hg4.x, hg4.y, hg4.z, hg4.w};
-            f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, t, 0, 0, 0);
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb < nmb) {
+        const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
+        const f16x8_t a0 = lds_frag<f16x8_t>(&Hl[buf][ao]);
+        const f16x8_t a1 = lds_frag<f16x8_t>(&Hl[buf][ao + 32]);
+        const f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const f32x4_t t = mfma(a1, b1, mfma(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f}));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) C.acc[mb][0][i] = fmaf(s, t[i], fmaf(bp, hgv[i], C.acc[mb][0][i]));
-          }
-        }
-        if (g + 1 < G) hstore(buf ^ 1);
-        if (g + 2 < G) hload(g + 2);
-        __syncthreads();
+        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(s, t[i], fmaf(bp, ag[i], acc[mb][i]));
       }
     }
+    astore(ic<(j + 1) % RA>{}, buf ^ 1);
+    aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, G - 1));
+    __syncthreads();
+  };
+  int g0 = 0;
+  for (; g0 + kRing <= G; g0 += kRing) {
+    step(ic<0>{}, g0);
+    step(ic<1>{}, g0 + 1);
+    step(ic<2>{}, g0 + 2);
+    step(ic<3>{}, g0 + 3);
   }
-  float* out = (T.e >= 0) ? A.expert_out : A.shared_out;
+  if (g0 < G) step(ic<0>{}, g0);
+  if (g0 + 1 < G) step(ic<1>{}, g0 + 1);
+  if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
+  float* out = shared ? A.shared_out : A.expert_out;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mb + 4 * (lane >> 4) + i;
-      if (r < T.mrows) out[(size_t)(T.m0 + r) * A.d + nb * 64 + 16 * wave + (lane & 15)] = C.acc[mb][0][i] / rowsc[r];
+      if (r < T.mrows) out[(size_t)(T.m0 + r) * A.d + nb * 64 + 16 * wave + (lane & 15)] = acc[mb][i] * rowinv[r];
     }
+}
+
+// Persistent over the work items, as the gate/up kernel.
+__global__ __launch_bounds__(256, 2) void k_prefill_down(PrefillArgs A) {
+  __shared__ DownSmem S;
+  TileMap M;
+  const int nrt = A.routed_mtiles > 0 ? tile_map_init(A, M) : 0;
+  const int nc = A.d / 64;
+  const int ns = xcd_blocks(A.shared_mtiles, nc);
+  const int n = ns + xcd_blocks(nrt, nc);
+  for (int item = blockIdx.x; item < n; item += gridDim.x) {
+    const bool shared = item < ns;
+    int mt, nb;
+    MTile T;
+    if (shared) {
+      xcd_item(item, A.shared_mtiles, nc, mt, nb);
+      if (mt >= A.shared_mtiles) continue;
+      shared_tile(A, mt, T);
+    } else {
+      xcd_item(item - ns, nrt, nc, mt, nb);
+      if (mt >= nrt || !tile_at(A, M, mt, T)) continue;
+    }
+    down_tile(A, T, nb, shared, S);
+    __syncthreads();  // the next item reuses the LDS
+  }
 }
 
 }  // namespace qmoe
