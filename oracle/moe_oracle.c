@@ -102,9 +102,13 @@ void oracle_router_logits(const oq_mat* router, const double* x, const float* of
     for (int32_t e = 0; e < router->rows; ++e) logits[e] += (double)offset[e];
 }
 
-/* a ranks before b: larger logit first, ties to the lower expert id */
+/* a ranks before b: larger logit first, ties to the lower expert id. The pages
+   never meet a NaN logit; this oracle ranks a NaN below every number (as -inf),
+   which keeps the order total. */
+static double rank_key(double v) { return v != v ? -INFINITY : v; }
 static int ranks_before(const double* l, int a, int b) {
-  return l[a] > l[b] || (l[a] == l[b] && a < b);
+  const double va = rank_key(l[a]), vb = rank_key(l[b]);
+  return va > vb || (va == vb && a < b);
 }
 
 /* steps 4 and 5; gap = l_(k) - l_(k+1), the margin of the k-th pick (INFINITY if k == E) */

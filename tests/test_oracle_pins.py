@@ -174,6 +174,27 @@ def test_topk_brute_force_against_library_sort():
         assert gap == lg[order[k - 1]] - lg[order[k]]
 
 
+def test_topk_nan_logits_rank_last():
+    """A NaN logit ranks below every number, ties by id (the reading for non-finite
+    activations): brute force against a library sort with NaN replaced by -inf."""
+    rng = np.random.default_rng(9)
+    for trial in range(100):
+        E, k = 64, 8
+        lg = rng.standard_normal(E) * 10
+        lg[rng.integers(0, E, trial % 70)] = np.nan
+        if trial % 5 == 0:
+            lg[rng.integers(0, E, 4)] = -np.inf
+        key = np.where(np.isnan(lg), -np.inf, lg)
+        order = np.lexsort((np.arange(E), -key))
+        idx, p, gap = O.topk_softmax(lg, k)
+        np.testing.assert_array_equal(idx, order[:k])
+        assert len(set(idx.tolist())) == k
+    idx, _, _ = O.topk_softmax(np.full(16, np.nan), 4)
+    np.testing.assert_array_equal(idx, [0, 1, 2, 3])
+    idx, _, _ = O.topk_softmax(np.array([np.nan, 1.0, np.nan, 3.0, -np.inf]), 3)
+    np.testing.assert_array_equal(idx, [3, 1, 0])  # NaN at id 0 ties the -inf at id 4; lower id first
+
+
 def test_topk_relabelling_permutes_selection():
     rng = np.random.default_rng(7)
     lg = rng.standard_normal(128)
