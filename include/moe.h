@@ -192,7 +192,9 @@ moe_status moe_expert_ffn_prefill_chunk(const moe_shape* shape, const moe_layer*
  * expert_out[r*top_k + j] (inv_perm == NULL; decode has rows == 1), summed in
  * slot order. y fp32 [rows][d_model]. If residual_bf16 is not NULL it is a
  * bf16 [rows][d_model] in/out buffer: residual = bf16_rne(fp32(residual) + y)
- * (the residual add between stacked layers).
+ * (the residual add between stacked layers). It may be the buffer x itself
+ * (bf16 x): every read of x precedes the residual store, here and in the
+ * fused layer calls below.
  */
 moe_status moe_combine(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                        int32_t rows, const float* expert_out, const int32_t* inv_perm, const float* topk_w,

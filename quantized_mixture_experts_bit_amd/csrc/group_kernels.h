@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ share
   float v = shared_out[(size_t)r * d + n];
   for (int k = 0; k < top_k; ++k) {
     const int pos = inv_perm ? inv_perm[r * top_k + k] : r * top_k + k;
+    if (pos < 0) continue;  // a pair the grouping dropped (invalid id, already reported)
     v = fmaf(topk_w[r * top_k + k], expert_out[(size_t)pos * d + n], v);
   }
   y[(size_t)r * d + n] = v;

@@ -27,8 +27,12 @@ __device__ __forceinline__ double ld_agent_d(const double* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// a beats b: larger logit, ties to the lower expert id
+// a beats b: larger logit, ties to the lower expert id. A NaN logit ranks below
+// every number (as -inf), so this is a strict total order on (logit, id) and the
+// picks are always k distinct valid ids, whatever the activations hold.
 __device__ __forceinline__ bool beats(double va, int ea, double vb, int eb) {
+  va = va != va ? -INFINITY : va;
+  vb = vb != vb ? -INFINITY : vb;
   return va > vb || (va == vb && ea < eb);
 }
 
