@@ -6,7 +6,8 @@ d_model 2816, 128 experts of d_ff 704 with 4-bit affine group-64 weights, shared
 expert d_ff 2112, 8-bit router, top-8), with the fraction of the HBM roofline
 on active-expert bytes. The 128-row prefill chunk (Zipf-skewed routing) is
 measured in the same run and reported under "prefill" with its roofline and
-MFMA utilisation; the 30-layer stacks under "stack" when --stack is given.
+MFMA utilisation, and the 30-layer stacks (decode 1 row, prefill chunks of 256
+rows, residual add between layers) under "stack".
 
 Inputs are synthetic and seeded (see synth/): every step uses a different layer
 of a pool of independently drawn layers and a fresh activation row, so the
@@ -75,9 +76,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600, help="timed decode steps (prefill: steps/10 chunks)")
     ap.add_argument("--warmup", type=int, default=2, help="untimed graph replays before timing")
-    ap.add_argument("--layers", type=int, default=16, help="distinct seeded layers in the rotation pool")
+    ap.add_argument("--layers", type=int, default=30, help="distinct seeded layers in the pool (rotation and stacks)")
     ap.add_argument("--prefill-rows", type=int, default=128)
+    ap.add_argument("--stack-rows", type=int, default=256, help="rows per chunk of the 30-layer prefill stack")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the oracle's timed CPU sample")
     args = ap.parse_args()
@@ -117,7 +120,8 @@ def main():
     steps_per_graph = 4 * L
     n_x = steps_per_graph
     xs = torch.from_numpy(synth.make_x(shape, n_x, seed=1, dtype="bf16")).view(torch.bfloat16).to(dev)
-    ws = torch.empty(q.moe_workspace_bytes(shape, max(1, args.prefill_rows)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(q.moe_workspace_bytes(shape, max(1, args.prefill_rows, args.stack_rows)), dtype=torch.uint8,
+                     device=dev)
     q.moe_workspace_init(ws)
     idx = torch.empty(n_x, k, dtype=torch.int32, device=dev)
     w = torch.empty(n_x, k, dtype=torch.float32, device=dev)
@@ -221,6 +225,108 @@ def main():
         log("prefill: %d rows, %.1f us/chunk, %.0f tok/s, roofline frac %.3f, MFMA util %.3f, %.1f distinct experts"
             % (R, p_ms * 1e3, prefill["value"], prefill["roofline"]["frac"], prefill["mfma_util"], distinct))
 
+    # ---------------------------------------------------------------- 30-layer stacks
+    stack = None
+    if not args.no_stack:
+        NL = min(30, L)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # decode: one row through NL layers, x <- bf16(x + y) in place after each
+        x0d = torch.from_numpy(synth.make_x(shape, 1, seed=41, dtype="bf16")).view(torch.bfloat16).to(dev)
+        hd = x0d.clone()
+        sid, sw = torch.empty(NL, k, dtype=torch.int32, device=dev), torch.empty(NL, k, device=dev)
+        syd = torch.empty(1, d, device=dev)
+
+        def stack_decode():
+            hd.copy_(x0d)
+            for l in range(NL):
+                q.moe_layer_decode(shape, dls[l].c, hd, None, sid[l], sw[l], eo, syd, hd, ws)
+
+        stack_decode()
+        torch.cuda.synchronize()
+        gsd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gsd, stream=cap):
+            stack_decode()
+        sd_rep = max(2, args.steps // NL)
+        for _ in range(args.warmup):
+            gsd.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(sd_rep):
+            gsd.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        sd_ms = ev0.elapsed_time(ev1) / sd_rep
+        sd_bytes = NL * dbytes
+        # prefill: chunks of RS rows through NL layers, Zipf-skewed routing per layer
+        RS = args.stack_rows
+        x0p = torch.from_numpy(synth.make_x(shape, RS, seed=42, dtype="bf16")).view(torch.bfloat16).to(dev)
+        hp = x0p.clone()
+        zl = [torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=l)).to(dev) for l in range(NL)]
+        s_idx = torch.empty(RS, k, dtype=torch.int32, device=dev)
+        s_w = torch.empty(RS, k, device=dev)
+        s_cnt = torch.empty(NL, E, dtype=torch.int32, device=dev)
+        s_off = torch.empty(NL, E + 1, dtype=torch.int32, device=dev)
+        s_perm = torch.empty(RS * k, dtype=torch.int32, device=dev)
+        s_inv = torch.empty(RS * k, dtype=torch.int32, device=dev)
+        s_eo = torch.empty(RS * k, d, device=dev)
+        s_y = torch.empty(RS, d, device=dev)
+
+        def stack_prefill():
+            hp.copy_(x0p)
+            for l in range(NL):
+                q.moe_layer_prefill(shape, dls[l].c, hp, RS, zl[l], s_idx, s_w, s_cnt[l], s_off[l], s_perm, s_inv,
+                                    s_eo, s_y, hp, ws)
+
+        stack_prefill()
+        torch.cuda.synchronize()
+        assert q.moe_check_device_error() == 0
+        s_counts = s_cnt.cpu().numpy()
+        gsp = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gsp, stream=cap):
+            stack_prefill()
+        sp_rep = max(2, args.steps // 100)
+        for _ in range(args.warmup):
+            gsp.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(sp_rep):
+            gsp.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        sp_ms = ev0.elapsed_time(ev1) / sp_rep
+        sp_ideal = [prefill_roofline(shape, s_counts[l], RS) for l in range(NL)]
+        sp_t = sum(t for t, _, _ in sp_ideal)
+        sp_fl = sum(fl for _, fl, _ in sp_ideal)
+        sp_by = sum(by for _, _, by in sp_ideal)
+        stack = {
+            "decode": {
+                "workload": "%d-layer stack of the same block (distinct seeded layers, %d experts each resident in "
+                            "one pool behind per-layer slot tables), decode 1 row, in-place residual "
+                            "x <- bf16(x + y) between layers; one HIP graph per token" % (NL, E),
+                "metric": "tokens/s through the %d-layer stack (decode bs=1)" % NL,
+                "value": 1000.0 / sd_ms, "unit": "tokens/s", "ms_per_token": sd_ms, "tokens": sd_rep,
+                "roofline": {"bound": "hbm", "algorithmic_bytes_per_token": sd_bytes,
+                             "achieved": sd_bytes / (sd_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                             "frac": sd_bytes / (sd_ms * 1e-3) / HBM_PEAK},
+            },
+            "prefill": {
+                "workload": "%d-layer stack, prefill chunks of %d rows, Zipf(1.1)-skewed router logits per layer, "
+                            "in-place residual; one HIP graph per chunk" % (NL, RS),
+                "metric": "tokens/s through the %d-layer stack (prefill chunk %d)" % (NL, RS),
+                "value": RS / (sp_ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": sp_ms, "chunks": sp_rep,
+                "roofline": {"bound": "sum over layers and GEMMs of max(bytes/HBM, flops/MFMA)",
+                             "ideal_ms": sp_t * 1e3, "frac": sp_t / (sp_ms * 1e-3)},
+                "mfma_util": sp_fl / (sp_ms * 1e-3) / MFMA_F16_PEAK,
+                "algorithmic_bytes": sp_by, "algorithmic_flops": sp_fl,
+                "distinct_experts_per_layer": [int(v) for v in (s_counts > 0).sum(1)],
+            },
+        }
+        log("stack decode: %d layers, %.1f us/token, %.0f tok/s, %.1f%% of HBM peak on active bytes"
+            % (NL, sd_ms * 1e3, 1000.0 / sd_ms, 100 * stack["decode"]["roofline"]["frac"]))
+        log("stack prefill: %d layers x %d rows, %.2f ms/chunk, %.0f tok/s, roofline frac %.3f, MFMA util %.3f"
+            % (NL, RS, sp_ms, stack["prefill"]["value"], stack["prefill"]["roofline"]["frac"],
+               stack["prefill"]["mfma_util"]))
+
     # ---------------------------------------------------------------- CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -271,6 +377,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "stack": stack,
     }
     print(json.dumps(out), flush=True)
 
