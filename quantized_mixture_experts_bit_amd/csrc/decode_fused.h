@@ -118,6 +118,14 @@ __device__ __forceinline__ const uint8_t* wait_ticket(const uint8_t* pool, uint3
   return pool + (uint64_t)(lo - 1) * 256;
 }
 
+// unsigned key with the order of beats() on the logit part: NaN as -inf, -0 as +0
+__device__ __forceinline__ uint64_t order_key(double v) {
+  if (v != v) v = -INFINITY;
+  v += 0.0;  // -0 -> +0
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
 struct FusedArgs {
   DecodeArgs A;              // weights, shapes, partial buffers, outputs
   const uint8_t* router_blob;
@@ -130,20 +138,38 @@ struct FusedArgs {
   int n_rt, n_sg, n_rg, n_sd, n_rd;
 };
 
-// vector operand held in LDS as hi/lo bf16 pairs starting at pair index `base`
-struct VecLDS {
-  const uint32_t* hh;
-  const uint32_t* hl;
-  int base;
-  __device__ __forceinline__ uint32_t hi(int p) const { return hh[p - base]; }
-  __device__ __forceinline__ uint32_t lo(int p) const { return hl[p - base]; }
-  static constexpr bool kLo = true;
-};
-struct LdsGroupSum {
-  const float* gs;
-  int base;
-  __device__ __forceinline__ float operator()(int g, int) const { return gs[g - base]; }
-};
+// group_dot with the vector operand in LDS as 32 hi and 32 lo pairs (hh, hl point at
+// the group's pair 0): the pairs are read in two batches of 16, one LDS wait each,
+// and accumulated in the same order as group_dot, so the result is the same
+__device__ __forceinline__ float group_dot_lds(const uint32_t* hh, const uint32_t* hl, uint4 qa, uint4 qb,
+                                               uint32_t sbw, float Vg) {
+  const uint32_t words[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+  float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint4 h4[4], l4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h4[i] = *reinterpret_cast<const uint4*>(hh + 16 * half + 4 * i);
+      l4[i] = *reinterpret_cast<const uint4*>(hl + 16 * half + 4 * i);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t w = words[4 * half + jj];
+      const uint32_t hv[4] = {h4[jj].x, h4[jj].y, h4[jj].z, h4[jj].w};
+      const uint32_t lv[4] = {l4[jj].x, l4[jj].y, l4[jj].z, l4[jj].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t p = nib_pair(w, t);
+        acc4[t] = dot2(p, hv[t], acc4[t]);
+        acc4[t] = dot2(p, lv[t], acc4[t]);
+      }
+    }
+  }
+  const float a = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+  const float s = bf16_lo(sbw), b = bf16_hi(sbw);
+  return fmaf(s, a, fmaf(-128.0f, s, b) * Vg);
+}
 
 // weights of one 64-row block for groups g0 + wave + 4i (i < GW), loaded ahead of use
 template <int GW>
@@ -162,13 +188,14 @@ struct RowLoads {
       }
     }
   }
-  template <typename V, typename VG>
-  __device__ __forceinline__ float dot(int g0, int g1, int wave, int lane, const V& v, const VG& vg) const {
+  // against h in LDS: pairs of group g at hh/hl + (g - g0) * 32, group sums at gs[g - g0]
+  __device__ __forceinline__ float dot_lds(int g0, int g1, int wave, const uint32_t* hh, const uint32_t* hl,
+                                           const float* gs) const {
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
       const int g = g0 + wave + 4 * i;
-      if (g < g1) acc += group_dot(v, g, qa[i], qb[i], sb[i], vg(g, lane));
+      if (g < g1) acc += group_dot_lds(hh + (g - g0) * 32, hl + (g - g0) * 32, qa[i], qb[i], sb[i], gs[g - g0]);
     }
     return acc;
   }
@@ -182,8 +209,9 @@ struct FusedSmem {
   int sel_e[16];
   int rank[4][256];
   float redf[4][64];
-  uint32_t hh[12 * 32];  // h hi pairs for up to 12 groups
-  uint32_t hl[12 * 32];
+  uint32_t slots[256];   // the layer's slot table (last router workgroup)
+  __attribute__((aligned(16))) uint32_t hh[12 * 32];  // h hi pairs for up to 12 groups
+  __attribute__((aligned(16))) uint32_t hl[12 * 32];
   float hsum[12];
   int last;
 };
@@ -231,8 +259,9 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
   }
   __syncthreads();
   if (!S.last) return;
-  // last router workgroup: full logits (tpe threads per expert, loads in flight together)
-  if (tid < 16) S.sel_e[tid] = -1;  // stays -1 only if the logits are not ordered (NaN)
+  // last router workgroup: the slot table (read while the partials arrive), the full
+  // logits (tpe threads per expert, loads in flight together), the ranking, the tickets
+  const uint32_t slot_entry = tid < E ? A.slot_table[tid] : 0u;
   const int tpe = 256 / E;
   const int e = tid % E, sub = tid / E;
   double part = 0.0;
@@ -255,24 +284,34 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
     S.lg[tid] = l;
   }
   __syncthreads();
-  // rank = number of experts that beat this one. Wave w counts the competitors in its
-  // quarter of the experts for every expert (lane + 64 j), partial ranks meet in LDS.
+  // Ranks by integer keys: a monotone map of the logit (NaN taken as -inf, -0 as +0)
+  // to an unsigned 64-bit key, ties broken by id: the order of beats(), strict and
+  // total, so the ranks are a permutation. With 256 / E threads per expert, each
+  // counts the competitors in its share that rank before its expert, reading their
+  // keys 16 at a time (one LDS wait per batch).
+  uint64_t* key = reinterpret_cast<uint64_t*>(S.xs);  // xs is free now
+  if (tid < E) {
+    key[tid] = order_key(S.lg[tid]);
+    S.slots[tid] = slot_entry;
+  }
+  __syncthreads();
   {
-    const int q0 = wave * (E / 4), q1 = q0 + E / 4;
-    for (int j = 0; j < E / 64; ++j) {
-      const int t = lane + 64 * j;
-      const double mine = S.lg[t];
-      int r = 0;
-      for (int e2 = q0; e2 < q1; e2 += 8) {
+    const int parts = 256 / E, h = tid / E, per = E / parts, me = tid % E;
+    const uint64_t mine = key[me];
+    int r = 0;
+    for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
+      uint64_t kk[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r += beats(S.lg[e2 + i], e2 + i, mine, t) ? 1 : 0;
-      }
-      S.rank[wave][t] = r;
+      for (int i = 0; i < 16; ++i) kk[i] = key[c0 + i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r += (kk[i] > mine || (kk[i] == mine && c0 + i < me)) ? 1 : 0;
     }
+    S.rank[h][me] = r;
   }
   __syncthreads();
   if (tid < E) {
-    const int rank = (S.rank[0][tid] + S.rank[1][tid]) + (S.rank[2][tid] + S.rank[3][tid]);
+    int rank = 0;
+    for (int h = 0; h < 256 / E; ++h) rank += S.rank[h][tid];
     if (rank < A.top_k) {
       S.sel_e[rank] = tid;
       S.sel_v[rank] = S.lg[tid];
@@ -291,7 +330,14 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
     if (t < k) {
       const int ei = S.sel_e[t];
       const float wv = (float)(ext / sum);
-      const uint8_t* blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, ei, E);
+      const uint8_t* blob = nullptr;  // as expert_blob, from the table read above
+      if (ei < 0 || ei >= E) {
+        flag_device_error(2u);
+      } else if ((uint64_t)S.slots[ei] >= A.n_blobs) {
+        flag_device_error(1u);
+      } else {
+        blob = A.pool + (uint64_t)S.slots[ei] * A.stride;
+      }
       const uint32_t lo = blob ? (uint32_t)((uint64_t)(blob - A.pool) / 256 + 1) : 0xffffffffu;
       ticket = ((uint64_t)__float_as_uint(wv) << 32) | lo;
       if (lane < 16) {
@@ -477,7 +523,7 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, bool route
   build_h(A, slot, g0, g1, S);
   float acc = 0.0f;
   if (rowblock)
-    acc = w.dot(g0, g1, wave, lane, VecLDS{S.hh, S.hl, g0 * 32}, LdsGroupSum{S.hsum, g0});
+    acc = w.dot_lds(g0, g1, wave, S.hh, S.hl, S.hsum);
   const float r = reduce_waves4(acc, S.redf, wave, lane);
   if (wave == 0) {
     const int n = nb * 64 + lane;
@@ -492,10 +538,23 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, bool route
 
 // ------------------------------------------------------------------ the kernel
 
+// Work item of a block. Blocks are dealt to the XCDs round robin (block b on XCD
+// b % 8) and the XCDs start the launch one after another, the last several
+// microseconds after the first; the router items head the dependency chain, so
+// they take blocks 0, 8, 16, ... (the first XCD) and the
+// other items the rest in order. Any placement is correct (all blocks are resident at once); this one is
+// faster.
+__device__ __forceinline__ int item_of_block(int b, int n_rt) {
+  if ((int)gridDim.x < 8 * n_rt) return b;  // too few blocks to spread: identity
+  if ((b & 7) == 0 && (b >> 3) < n_rt) return b >> 3;
+  const int before = min(n_rt, (b + 7) >> 3);  // router blocks below b
+  return n_rt + b - before;
+}
+
 template <typename XT>
 __global__ __launch_bounds__(256, 6) void k_decode_fused(FusedArgs F, const XT* __restrict__ x) {
   __shared__ FusedSmem S;
-  int b = blockIdx.x;
+  int b = item_of_block(blockIdx.x, F.n_rt);
   if (b < F.n_rt) return fused_router(F, x, b, S);
   b -= F.n_rt;
   // one call site per item kind, so each body is inlined once
