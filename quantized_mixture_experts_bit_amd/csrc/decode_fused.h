@@ -118,14 +118,6 @@ __device__ __forceinline__ const uint8_t* wait_ticket(const uint8_t* pool, uint3
   return pool + (uint64_t)(lo - 1) * 256;
 }
 
-// unsigned key with the order of beats() on the logit part: NaN as -inf, -0 as +0
-__device__ __forceinline__ uint64_t order_key(double v) {
-  if (v != v) v = -INFINITY;
-  v += 0.0;  // -0 -> +0
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-
 struct FusedArgs {
   DecodeArgs A;              // weights, shapes, partial buffers, outputs
   const uint8_t* router_blob;
@@ -284,39 +276,15 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
     S.lg[tid] = l;
   }
   __syncthreads();
-  // Ranks by integer keys: a monotone map of the logit (NaN taken as -inf, -0 as +0)
-  // to an unsigned 64-bit key, ties broken by id: the order of beats(), strict and
-  // total, so the ranks are a permutation. With 256 / E threads per expert, each
-  // counts the competitors in its share that rank before its expert, reading their
-  // keys 16 at a time (one LDS wait per batch).
+  // the ranking (rank_topk: integer order keys, ties by id) and the picks' logits
   uint64_t* key = reinterpret_cast<uint64_t*>(S.xs);  // xs is free now
   if (tid < E) {
     key[tid] = order_key(S.lg[tid]);
     S.slots[tid] = slot_entry;
   }
   __syncthreads();
-  {
-    const int parts = 256 / E, h = tid / E, per = E / parts, me = tid % E;
-    const uint64_t mine = key[me];
-    int r = 0;
-    for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
-      uint64_t kk[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) kk[i] = key[c0 + i];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) r += (kk[i] > mine || (kk[i] == mine && c0 + i < me)) ? 1 : 0;
-    }
-    S.rank[h][me] = r;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int rank = 0;
-    for (int h = 0; h < 256 / E; ++h) rank += S.rank[h][tid];
-    if (rank < A.top_k) {
-      S.sel_e[rank] = tid;
-      S.sel_v[rank] = S.lg[tid];
-    }
-  }
+  rank_topk(key, E, A.top_k, S.rank, S.sel_e);
+  if (tid < A.top_k) S.sel_v[tid] = S.lg[S.sel_e[tid]];
   __syncthreads();
   if (wave == 0) {
     const int k = A.top_k;

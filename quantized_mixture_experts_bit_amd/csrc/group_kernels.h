@@ -12,66 +12,110 @@
 
 namespace qmoe {
 
-// One wavefront. Thread t owns pairs [t*chunk, (t+1)*chunk) in order; cnt[e][t]
-// counts them per expert, is turned into per-(expert, thread) start positions
-// by an exclusive scan in (expert, thread) order, and every thread then places
-// its own pairs in order: a stable counting sort, bit-exact.
-__global__ __launch_bounds__(64) void k_group(const int32_t* __restrict__ topk_idx, int n_pairs, int n_experts,
-                                              int32_t* __restrict__ count, int32_t* __restrict__ offset,
-                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
-  extern __shared__ uint16_t cnt[];  // [n_experts][64]
-  __shared__ int32_t tot[257];
-  const int t = threadIdx.x;
-  const int chunk = (n_pairs + 63) / 64;
-  for (int i = t; i < n_experts * 64; i += 64) cnt[i] = 0;
+// Lanes of the wavefront holding the same expert id as this lane (ids < 256: one
+// ballot per id bit); only lanes with `valid` set take part.
+__device__ __forceinline__ uint64_t match_lanes(int e, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t on = __ballot(bit);
+    m &= bit ? on : ~on;
+  }
+  return m;
+}
+
+constexpr int kGroupWaves = 16;  // one workgroup of 1024 threads
+
+// Stable counting sort of the (row, slot) pairs by expert, in one workgroup.
+// Wave w owns the pairs [w*S, (w+1)*S) (S a multiple of 64) and walks them 64 at
+// a time in order, so the pairs are visited in (wave, round, lane) = pair order.
+// Pass 1 counts each wave's pairs per expert (lanes with the same id are matched
+// with ballots; the lowest adds the group's size). Per expert, the wave counts are
+// scanned in wave order, and the totals across experts. Pass 2 walks the pairs
+// again: a pair's position is its expert's offset + the pairs of that expert in
+// earlier waves + those in earlier rounds of its wave (the running count) + the
+// matching lanes below it. The result is the order (expert, pair) exactly.
+__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ topk_idx, int n_pairs, int n_experts,
+                                                int32_t* __restrict__ count, int32_t* __restrict__ offset,
+                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  extern __shared__ int32_t cnt[];  // [kGroupWaves][n_experts]
+  __shared__ int32_t off[256];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int i = t; i < kGroupWaves * n_experts; i += 1024) cnt[i] = 0;
   __syncthreads();
-  const int p0 = t * chunk, p1 = min(n_pairs, p0 + chunk);
-  for (int p = p0; p < p1; ++p) {
-    const int e = topk_idx[p];
-    if (e < 0 || e >= n_experts) {  // not an expert id: reported, and the pair is dropped
+  const int S = ((n_pairs + kGroupWaves - 1) / kGroupWaves + 63) & ~63;
+  const int p_end = min(n_pairs, (w + 1) * S);
+  int32_t* mine = cnt + w * n_experts;
+  for (int p0 = w * S; p0 < p_end; p0 += 64) {
+    const int p = p0 + lane;
+    int e = p < p_end ? topk_idx[p] : -1;
+    if (p < p_end && (e < 0 || e >= n_experts)) {  // not an expert id: reported, and the pair is dropped
       flag_device_error(2u);
-      continue;
+      e = -1;
     }
-    cnt[e * 64 + t] += 1;
+    const bool valid = e >= 0;
+    const uint64_t m = match_lanes(e, valid);
+    if (valid && (m & below) == 0) mine[e] += __popcll(m);
   }
   __syncthreads();
-  for (int e = t; e < n_experts; e += 64) {
-    int s = 0;
-    for (int j = 0; j < 64; ++j) s += cnt[e * 64 + j];
-    tot[e] = s;
-  }
-  __syncthreads();
-  if (t == 0) {
+  // per expert: wave counts -> starts within the expert, in wave order
+  for (int e = t; e < n_experts; e += 1024) {
     int run = 0;
-    for (int e = 0; e < n_experts; ++e) {
-      const int c = tot[e];
-      count[e] = c;
-      offset[e] = run;
-      tot[e] = run;
+    for (int ww = 0; ww < kGroupWaves; ++ww) {
+      const int c = cnt[ww * n_experts + e];
+      cnt[ww * n_experts + e] = run;
       run += c;
     }
-    offset[n_experts] = run;
+    off[e] = run;  // total for now
   }
   __syncthreads();
-  for (int e = t; e < n_experts; e += 64) {
-    int run = tot[e];
-    for (int j = 0; j < 64; ++j) {
-      const int c = cnt[e * 64 + j];
-      cnt[e * 64 + j] = (uint16_t)run;  // starts fit: n_pairs < 65536 is checked on the host
-      run += c;
+  // exclusive scan of the totals over the experts (wave 0, four experts per lane)
+  if (w == 0) {
+    int v[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      v[j] = e < n_experts ? off[e] : 0;
+      local += v[j];
     }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - local;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      if (e < n_experts) {
+        count[e] = v[j];
+        offset[e] = run;
+        off[e] = run;
+      }
+      run += v[j];
+    }
+    if (lane == 63) offset[n_experts] = incl;
   }
   __syncthreads();
-  for (int p = p0; p < p1; ++p) {
-    const int e = topk_idx[p];
-    if (e < 0 || e >= n_experts) {
+  for (int p0 = w * S; p0 < p_end; p0 += 64) {
+    const int p = p0 + lane;
+    int e = p < p_end ? topk_idx[p] : -1;
+    if (e >= n_experts) e = -1;
+    const bool valid = e >= 0;
+    const uint64_t m = match_lanes(e, valid);
+    if (valid) {
+      const int pos = off[e] + mine[e] + __popcll(m & below);
+      perm[pos] = p;
+      inv_perm[p] = pos;
+    } else if (p < p_end) {
       inv_perm[p] = -1;
-      continue;
     }
-    const int pos = cnt[e * 64 + t];
-    cnt[e * 64 + t] = (uint16_t)(pos + 1);
-    perm[pos] = p;
-    inv_perm[p] = pos;
+    // every lane has read the running count above before the lowest lane of each
+    // group advances it (one wavefront, LDS operations in order)
+    if (valid && (m & below) == 0) mine[e] += __popcll(m);
   }
 }
 

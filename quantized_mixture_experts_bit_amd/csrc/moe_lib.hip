@@ -379,8 +379,8 @@ moe_status moe_group_by_expert(const moe_shape* s, const int32_t* idx, int32_t r
   (void)ws_bytes;
   if (!count || !offset) return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!idx || !perm || !inv_perm)) return MOE_ERR_INVALID_ARG;
-  const size_t lds = sizeof(uint16_t) * 64 * s->n_experts;
-  k_group<<<1, 64, lds, (hipStream_t)stream>>>(idx, rows * s->top_k, s->n_experts, count, offset, perm, inv_perm);
+  const size_t lds = sizeof(int32_t) * kGroupWaves * s->n_experts;
+  k_group<<<1, 1024, lds, (hipStream_t)stream>>>(idx, rows * s->top_k, s->n_experts, count, offset, perm, inv_perm);
   return launched();
 }
 
@@ -485,8 +485,8 @@ moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void*
     launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, nullptr, ws, hs);
   else
     launch_router(s, L, (const float*)x, rows, off, idx, w, nullptr, ws, hs);
-  const size_t lds = sizeof(uint16_t) * 64 * s->n_experts;
-  k_group<<<1, 64, lds, hs>>>(idx, rows * s->top_k, s->n_experts, count, offset, perm, inv_perm);
+  const size_t lds = sizeof(int32_t) * kGroupWaves * s->n_experts;
+  k_group<<<1, 1024, lds, hs>>>(idx, rows * s->top_k, s->n_experts, count, offset, perm, inv_perm);
   PrefillArgs A = prefill_args(s, L, rows, offset, perm, expert_out, ws);
   if (dt == MOE_BF16)
     launch_prefill(A, (const uint16_t*)x, true, true, hs);

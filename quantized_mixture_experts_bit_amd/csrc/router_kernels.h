@@ -36,11 +36,47 @@ __device__ __forceinline__ bool beats(double va, int ea, double vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
+// Unsigned key with the order of beats() on the logit part: NaN as -inf, -0 as +0.
+__device__ __forceinline__ uint64_t order_key(double v) {
+  if (v != v) v = -INFINITY;
+  v += 0.0;  // -0 -> +0
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Top-k of E keys (E <= 256, a multiple of 64) by rank, all 256 threads of the
+// workgroup: rank = the number of experts that beat this one under (key desc,
+// id asc), a strict total order, so the ranks are a permutation. 256 / E threads
+// per expert each count the competitors in their share, reading the keys 16 at a
+// time (one LDS wait per batch). Writes the ids of ranks 0..k-1 to sel_e[rank].
+// key, rank and sel_e are LDS; ends with a barrier.
+__device__ __forceinline__ void rank_topk(const uint64_t* key, int E, int k, int (*rank)[256], int* sel_e) {
+  const int tid = threadIdx.x;
+  const int parts = 256 / E, h = tid / E, per = E / parts, me = tid % E;
+  const uint64_t mine = key[me];
+  int r = 0;
+  for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
+    uint64_t kk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kk[i] = key[c0 + i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += (kk[i] > mine || (kk[i] == mine && c0 + i < me)) ? 1 : 0;
+  }
+  rank[h][me] = r;
+  __syncthreads();
+  if (tid < E) {
+    int rk = 0;
+    for (int j = 0; j < parts; ++j) rk += rank[j][tid];
+    if (rk < k) sel_e[rk] = tid;
+  }
+  __syncthreads();
+}
+
 // grid (n_experts/64, nsplit, ceil(rows/RPW)), block 256. Workgroup (nb, split, chunk):
 // lane = expert nb*64 + lane, wave w = groups [split*16 + 4w, +4) of the reduction,
 // rows [chunk*RPW, +RPW). Partial logits go to `partial` [nsplit][rows][E]; the
 // last workgroup of a row chunk (arrival counter) sums them in split order, adds
-// the offset and picks the top-k of each row of the chunk (one wave per row).
+// the offset and picks the top-k of each row of the chunk (rank_topk).
 template <typename XT, int RPW>
 __global__ __launch_bounds__(256) void k_router(const uint8_t* __restrict__ router, const XT* __restrict__ x,
                                                 int rows, int d, int n_experts, int top_k, int nsplit,
@@ -116,66 +152,41 @@ __global__ __launch_bounds__(256) void k_router(const uint8_t* __restrict__ rout
   __syncthreads();
   if (!last) return;
 
-  // ---- top-k + softmax for the chunk's rows, one wave per row
-  if (wave < nr) {
-    const int row = r0 + wave;
-    double l[4];
+  // ---- logits of the chunk's rows (partials summed in split order, + offset), then
+  // per row: ranking by all 256 threads and the softmax over the picks
+  __shared__ double lgv[RPW][256];
+  __shared__ uint64_t key[256];
+  __shared__ int rank[4][256];
+  __shared__ int sel_e[16];
+  for (int i = tid; i < nr * n_experts; i += 256) {
+    const int r = i / n_experts, e = i % n_experts, row = r0 + r;
+    double pv[kMaxRouterSplits];  // all loads in flight at once, summed in split order
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < n_experts) {
-        double pv[kMaxRouterSplits];  // all loads in flight at once, summed in split order
+    for (int sp = 0; sp < kMaxRouterSplits; ++sp)
+      pv[sp] = sp < nsplit ? ld_agent_d(&partial[((size_t)sp * rows + row) * n_experts + e]) : 0.0;
+    double a = 0.0;
 #pragma unroll
-        for (int sp = 0; sp < kMaxRouterSplits; ++sp)
-          pv[sp] = sp < nsplit ? ld_agent_d(&partial[((size_t)sp * rows + row) * n_experts + e]) : 0.0;
-        double a = 0.0;
-#pragma unroll
-        for (int sp = 0; sp < kMaxRouterSplits; ++sp) a += pv[sp];
-        if (offset) a += (double)offset[e];
-        l[j] = a;
-        if (logits_out) logits_out[(size_t)row * n_experts + e] = a;
-      } else {
-        l[j] = -INFINITY;
+    for (int sp = 0; sp < kMaxRouterSplits; ++sp) a += pv[sp];
+    if (offset) a += (double)offset[e];
+    lgv[r][e] = a;
+    if (logits_out) logits_out[(size_t)row * n_experts + e] = a;
+  }
+  for (int r = 0; r < nr; ++r) {
+    __syncthreads();  // lgv complete; the previous row's picks are read
+    if (tid < n_experts) key[tid] = order_key(lgv[r][tid]);
+    __syncthreads();
+    rank_topk(key, n_experts, top_k, rank, sel_e);
+    if (wave == 0) {
+      // softmax over the picks in pick order (fp64), fixed summation order
+      const int row = r0 + r;
+      const int se = lane < top_k ? sel_e[lane] : 0;
+      const double ex = lane < top_k ? exp(lgv[r][se] - lgv[r][sel_e[0]]) : 0.0;
+      double sum = 0.0;
+      for (int t = 0; t < top_k; ++t) sum += __shfl(ex, t, 64);
+      if (lane < top_k) {
+        topk_idx[(size_t)row * top_k + lane] = se;
+        topk_w[(size_t)row * top_k + lane] = (float)(ex / sum);
       }
-    }
-    double sel_v = 0.0;  // lane t < top_k keeps pick t
-    int sel_e = 0;
-    unsigned taken = 0;
-    double top = 0.0;
-    for (int t = 0; t < top_k; ++t) {
-      double bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        if (e < n_experts && !((taken >> j) & 1u) && beats(l[j], e, bv, be)) {
-          bv = l[j];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (beats(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (t == 0) top = bv;
-      if (lane == t) {
-        sel_v = bv;
-        sel_e = be;
-      }
-    }
-    // softmax over the picks in pick order (fp64), fixed summation order
-    const double ex = lane < top_k ? exp(sel_v - top) : 0.0;
-    double sum = 0.0;
-    for (int t = 0; t < top_k; ++t) sum += __shfl(ex, t, 64);
-    if (lane < top_k) {
-      topk_idx[(size_t)row * top_k + lane] = sel_e;
-      topk_w[(size_t)row * top_k + lane] = (float)(ex / sum);
     }
   }
   if (tid == 0) counters[chunk] = 0u;
