@@ -60,11 +60,23 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Sum over the 64 lanes of a wavefront, returned to every lane. DPP row operations
+// (pair and quad swaps, half-row and row mirrors, then the row broadcasts of lanes
+// 15 and 31) leave the total in lane 63, which is read out: a few VALU operations
+// instead of a chain of LDS-routed shuffles.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask,
+                                                                   0xf, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xf>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xf>(v);  // row_mirror: every lane of a row holds the row's sum
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast15 into rows 1 and 3
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
