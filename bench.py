@@ -71,6 +71,56 @@ def prefill_roofline(shape, counts, rows):
     return t, flops, nbytes
 
 
+CSRC = os.path.join(ROOT, "quantized_mixture_experts_bit_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_fused_gemma4_decode_traffic.txt")
+
+
+def csrc_digest():
+    """sha256 over the HIP sources (names and bytes, sorted): identifies the kernel build."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        p = os.path.join(CSRC, name)
+        if os.path.isfile(p) and name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per k_decode_fused launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE passes, each divided by the factor the same counter shows on a plain copy of
+    known size), or None when the summary is missing or the kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("csrc_sha256") != csrc_digest():
+        return None, "counters were taken on other kernel sources"
+    fetch = float(kv["fetch_bytes_per_launch"]) / float(kv["copy_factor_fetch"])
+    write = float(kv["write_bytes_per_launch"]) / float(kv["copy_factor_write"])
+    return fetch + write, {"fetch_bytes": fetch, "write_bytes": write, "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+
+
+def calibrate_copy(mbytes):
+    """A plain device copy of known size (for the counter calibration): src -> dst, 5 times."""
+    import torch
+    n = int(mbytes * 1e6) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,13 +132,18 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="rows in the oracle's timed CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=1536, help="rows in the oracle's timed CPU sample")
+    ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes 5 times (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy > 0:
+        return calibrate_copy(args.calibrate_copy)
 
     import numpy as np
     import torch
@@ -344,6 +399,7 @@ def main():
         log("cpu oracle: %d rows in %.1f s on %d threads -> %.2f tok/s" % (args.cpu_rows, dt, O.threads(),
                                                                            cpu["value"]))
 
+    traffic, traffic_detail = measured_traffic()
     out = {
         "metric": "MoE-layer tokens/s (decode bs=1)",
         "value": dec_tok_s,
@@ -372,7 +428,8 @@ def main():
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": dec_bw / HBM_PEAK,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_detail": traffic_detail,
             "algorithmic_bytes_per_launch": dbytes,
         },
         "cpu_baseline": cpu,
