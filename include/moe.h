@@ -27,7 +27,10 @@
  *   - The library allocates no device memory. Scratch space comes from the
  *     caller's workspace `ws` of `ws_bytes` bytes (>= moe_workspace_bytes()).
  *     The workspace must be zero-filled once before its first use
- *     (moe_workspace_init); every call leaves its counters at zero again.
+ *     (moe_workspace_init). Every call leaves it ready for the next one: the
+ *     arrival counters are back at zero, and the whole-block decode keeps a
+ *     call counter (epoch) there that tags its hand-off words, so the
+ *     workspace must not be overwritten between calls.
  *     Calls that overlap in time need separate workspaces.
  *   - Arguments are validated before anything is enqueued; a failing check
  *     returns a negative moe_status and launches nothing. No C++ exception

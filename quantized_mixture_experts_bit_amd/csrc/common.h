@@ -32,6 +32,7 @@ constexpr int kTile8Codes = 4096;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -53,6 +54,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int t) {
   return ((w >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
 }
+
+// nib_pair with its two constants held in registers (the mask in an SGPR, the exponent
+// bits in a VGPR): a pair is then one shift and one v_and_or_b32, where literal
+// operands cost a shift, an and and an or.
+struct NibK {
+  uint32_t mask, expo;
+  __device__ __forceinline__ NibK() {
+    asm("s_mov_b32 %0, 0xf000f" : "=s"(mask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(expo));
+  }
+  __device__ __forceinline__ uint32_t pair(uint32_t w, int t) const { return ((w >> (4 * t)) & mask) | expo; }
+};
 
 // tanh form of GELU (Hendrycks & Gimpel), fp32
 __device__ __forceinline__ float gelu_tanh(float z) {
@@ -77,6 +90,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   v = dpp_add<0x142, 0xa>(v);  // row_bcast15 into rows 1 and 3
   v = dpp_add<0x143, 0xc>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Maximum over the 64 lanes of a wavefront (unsigned), returned to every lane: the
+// DPP steps of wave_sum with max in place of add (rows outside a step's row mask keep
+// their value: the moved-in 0 is the identity of max on unsigned values).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xf, false);
+  return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max<0xB1, 0xf>(v);
+  v = dpp_max<0x4E, 0xf>(v);
+  v = dpp_max<0x141, 0xf>(v);
+  v = dpp_max<0x140, 0xf>(v);
+  v = dpp_max<0x142, 0xa>(v);
+  v = dpp_max<0x143, 0xc>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }

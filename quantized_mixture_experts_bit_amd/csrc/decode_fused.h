@@ -1,32 +1,41 @@
-// One decode row through the whole block in ONE persistent launch.
+// One decode row through the whole block in ONE launch.
 //
-// The block's dependency chain for one token is router -> top-k -> routed gate/up
-// -> GeGLU -> routed down -> combine, with the shared expert independent of the
-// routing (the pages run the shared-expert branch while the routed experts are
-// being fetched: blog-mushroom article "TurboFieldfare: Gemma 4 26B on an 8 GB
-// MacBook", section "Why 26B Fits in 2 GB"). Separate launches serialise every
-// step's latency; here the workgroups of one launch take work items in
-// dependency order (workgroup index = item index):
+// The dependency chain for one token is router -> top-k -> routed gate/up ->
+// GeGLU -> routed down -> combine. The shared expert does not depend on the
+// routing and streams from the start (the pages run the shared-expert branch
+// while the routed experts are being fetched: blog-mushroom article
+// "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook", section "Why 26B Fits in 2 GB").
 //
-//   [router partials | shared gate/up | routed gate/up | shared down | routed down]
+// Work items, one workgroup each, in dependency order (an item waits only for
+// items before it; the launch is used only when the whole grid is resident),
+// and a last workgroup that keeps the epoch (below):
+//   router       2 experts over the whole reduction, fp64          -> 2 logits
+//   shared g/u   16 rows of the shared gate and up matrices         -> 16 values of h
+//   routed g/u   (slot, 16 rows) of the slot's expert               -> 16 values of h
+//   routed down  (slot, 64 output rows) over the slot's whole h     -> 64 expert outputs
+//   shared down  (64 output rows, second half of the shared h)      -> 64 partial outputs
+//   combine      (64 output rows, first half of the shared h), then y for those rows
 //
-// and a workgroup that needs earlier results waits on a flag (bounded spin; a
-// timeout sets MOE_DEVERR_SYNC_TIMEOUT instead of hanging). Items wait only on
-// items with smaller indices, and the launch is only used when the whole grid
-// fits on the chip at once. Waiting items first issue every load that does not
-// depend on the awaited data: a routed down item streams its weights as soon as
-// the routing is known, before the GeGLU output exists.
-//   - router: fp64 partial logits of 64 experts x 4 groups; the last arriving
-//     router workgroup sums the partials, ranks all experts (logit desc, id asc),
-//     and publishes a routing record (picks, softmax weights, blob offsets);
-//   - gate/up: (slot, matrix, 64-row block, reduction part) -> fp32 partials;
-//   - down: the item rebuilds h = gelu(gate) * up for its reduction range from the
-//     partials (fixed order), then runs the 4-bit GEMV; the last of the
-//     top_k + Ps items of each 64-row output block forms y (+ residual).
-// Hand-offs use sc1 stores/loads (see common.h), never L2 flushes. Anything many
-// workgroups poll or read is replicated 16 times, 4 KiB apart, so the readers
-// spread over memory channels instead of queueing on one line, and arrival
-// counters are two-level so no counter takes more than a few dozen atomics.
+// A hand-off between workgroups goes through the coherence point the XCDs share
+// and costs about a microsecond, so the chain is cut to the fewest hand-offs:
+//   - there is no ranking workgroup: every routed item and every combine reads
+//     the logits and ranks the experts itself (logit desc, id asc) on unique
+//     31-bit keys with independent compares, checked exact around the picks;
+//   - a gate/up item covers the whole reduction of its rows, so h needs no
+//     partial sums and no separate GeGLU step;
+//   - every hand-off is a set of 64-bit words (32-bit payload, 32-bit tag), each
+//     written by one agent-scope store; a reader polls the words it needs until
+//     all carry this call's tag. No arrival counters, flags or fences sit on
+//     the path. Words that many readers need (logits, h) are written
+//     in several copies some kilobytes apart, so the polling does not pile onto
+//     a few channels.
+// The tag is the call's epoch + 1. Every workgroup reads the epoch (one of
+// several copies) when it starts and, once it has it, adds one to an arrival
+// counter without waiting for the result. One extra workgroup, the last of the
+// grid, waits until every other workgroup has arrived, then advances the epoch
+// for the next call and clears the counters: nothing reads the epoch after that.
+// Waits are bounded: a timeout sets MOE_DEVERR_SYNC_TIMEOUT instead of hanging
+// (the workspace must then be re-initialised).
 #pragma once
 
 #include "common.h"
@@ -35,7 +44,63 @@
 
 namespace qmoe {
 
-constexpr int kSpinLimit = 1 << 20;  // polls (~1 us each) before a wait gives up
+constexpr int kSpinLimit = 1 << 20;  // polling rounds (about a microsecond each) before a wait gives up
+constexpr int kFusedRows = 16;       // gate/up rows per item
+constexpr int kFusedRouterE = 2;     // experts per router item
+constexpr int kLgCopies = 16;        // copies of the logits ...
+constexpr int kLgStride = 1024;      // ... 8 KiB apart (words)
+constexpr int kHCopies = 4;          // copies of h
+constexpr int kSyncLine = 32;        // words per 128-byte line: one sync word per line
+constexpr int kEpochCopies = 64;     // epoch copy c at line c
+constexpr int kArrivalCounters = 32; // arrival counter i at line kEpochCopies + i
+constexpr int kFusedSyncWords = (kEpochCopies + kArrivalCounters) * kSyncLine;
+constexpr int kFusedXWords = 3072;   // LDS words holding x (or h as hi and lo bf16 halves)
+constexpr int kFusedMaxG = 48;       // d_model / 64
+constexpr int kFusedGuI = 6;         // gate/up loads per lane and matrix: group pairs / 4 waves
+constexpr int kFusedRoutedGW = 3;    // routed down: groups of d_ff per wave (d_ff <= 768)
+constexpr int kFusedSharedGW = 5;    // shared down: groups of half of d_ff_shared per wave (<= 2560)
+
+struct FusedArgs {
+  const uint8_t* pool;
+  uint64_t stride, n_blobs;
+  const uint32_t* slot_table;
+  const uint8_t* router_blob;
+  const uint8_t* shared_blob;
+  const float* offset;  // [E] or null
+  int d, f, fs, E, top_k, fmax;
+  int32_t* idx_out;     // [top_k]
+  float* w_out;         // [top_k]
+  float* expert_out;    // [top_k][d], unweighted
+  float* y;             // [d]
+  uint16_t* residual;   // [d] bf16 or null: residual <- bf16(residual + y)
+  uint64_t* lg_tag;     // kLgCopies x kLgStride: fp64 logits as (low, high) 32-bit halves
+  uint64_t* h_tag;      // kHCopies x [(top_k + 1) * fmax] (h_stride apart): GeGLU outputs of the routed
+                        // slots, then the shared expert
+  uint64_t h_stride;
+  uint64_t* eo_tag;     // [(top_k + 1) * d]: routed expert outputs, then the shared expert's second half
+  uint32_t* sync;       // kFusedSyncWords
+  int n_rt, n_sg, n_rg, n_rd, n_sd;  // n_sd = d / 64 second-half items, then as many combines
+};
+
+struct FusedSmem {
+  __attribute__((aligned(16))) uint32_t xb[kFusedXWords];  // x pairs (or values), or h hi | lo pairs
+  float xg[2 * kFusedMaxG];  // sums of x over 32-column halves of each group
+  float hsum[48];            // sums of h (hi + lo) per group
+  float red[2][4][64];
+  double rd[256];
+  double lg[256];
+  uint64_t key[256];
+  uint32_t lgw[512];
+  uint32_t kp[256];
+  int rank[4][256];
+  uint32_t slots[256];
+  float eo[17][64];
+  float gu[2][kFusedRows];
+  float hv[kFusedRows];
+  double lgv[kFusedRouterE];
+  int sel_e[17];
+  float selw[16];
+};
 
 __device__ __forceinline__ uint32_t ld_agent_u(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -43,100 +108,392 @@ __device__ __forceinline__ uint32_t ld_agent_u(const uint32_t* p) {
 __device__ __forceinline__ void st_agent_u(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Thread 0 spins until *p >= target; then the whole workgroup proceeds.
-__device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target) {
-  if (threadIdx.x == 0) {
-    int it = 0;
-    while (ld_agent_u(p) < target) {
-      if (++it > kSpinLimit) {
-        flag_device_error(4u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  __syncthreads();
-  asm volatile("" ::: "memory");
+__device__ __forceinline__ void put_tag(uint64_t* p, uint32_t payload, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Sync words (uint32) in the workspace:
-//   [0, 4096)       counters: router, shared, per-slot, per-output-block combine, done,
-//                   and level-1 counters per (slot, 64-row block) from kL1
-//   flags           (2 + 16) kinds x kCopies copies, kStride words apart
-//   records         kCopies copies of the routing record, kStride words apart
-struct FusedSync {
-  static constexpr int kRouter = 0, kShared = 1, kSlot0 = 2, kL1 = 256;
-  static constexpr int kCopies = 16, kStride = 1024;
-  static constexpr int kFlagBase = 4096;
-  static constexpr int kRecBase = kFlagBase + (2 + 16) * kCopies * kStride;
-  static constexpr int kWords = kRecBase + kCopies * kStride;
-  __device__ static int combine(int top_k, int nb) { return kSlot0 + top_k + nb; }
-  __device__ static int done(int top_k, int nbd) { return kSlot0 + top_k + nbd; }
-  // flags: 1 = shared gate/up done, 2 + slot = routed slot done (0 unused)
-  __device__ static int flag(int f, int copy) { return kFlagBase + (f * kCopies + copy) * kStride; }
-  // routing record copy: one 64-bit ticket per slot (16 slots), 0 until published:
-  // low word = blob offset / 256 + 1 (all ones: no blob), high word = softmax weight bits
-  __device__ static int rec(int copy) { return kRecBase + copy * kStride; }
-};
-constexpr int kFusedSyncWords = FusedSync::kWords;
-
-__device__ __forceinline__ void raise_flag(uint32_t* sync, int f) {
-  for (int c = 0; c < FusedSync::kCopies; ++c) st_agent_u(&sync[FusedSync::flag(f, c)], 1u);
-}
-__device__ __forceinline__ void wait_flag(const uint32_t* sync, int f) {
-  wait_counter(&sync[FusedSync::flag(f, blockIdx.x % FusedSync::kCopies)], 1u);
-}
-__device__ __forceinline__ uint64_t* my_record(uint32_t* sync) {
-  return reinterpret_cast<uint64_t*>(sync + FusedSync::rec(blockIdx.x % FusedSync::kCopies));
-}
-__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
+__device__ __forceinline__ uint64_t get_tag(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Thread 0 polls the slot's ticket (one 64-bit load: readiness and payload arrive together);
-// returns the expert blob (nullptr if the pick had no valid blob) to every thread.
-__device__ __forceinline__ const uint8_t* wait_ticket(const uint8_t* pool, uint32_t* sync, int slot) {
-  __shared__ uint64_t tk;
-  if (threadIdx.x == 0) {
-    const uint64_t* p = my_record(sync) + slot;
-    uint64_t v = ld_agent_u64(p);
-    int it = 0;
-    while (v == 0) {
-      if (++it > kSpinLimit) {
-        flag_device_error(4u);
-        v = 0xffffffffull;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-      v = ld_agent_u64(p);
-    }
-    tk = v;
+
+// Every thread of the workgroup calls this. Polls the n tagged words at addr(i)
+// (thread t takes i = t + 256 j, j < N; words with skip(i) are not read) until all
+// carry `tag`, then hands each payload to use(i, payload). The loads of one round
+// are in flight together; a round reloads only the words not yet in. after_first()
+// runs once the first round's loads are issued, before their results are waited
+// for (stores issued there are not waited for by this poll).
+// on_first_in(): if kWatch, runs once, after the first round in which some word came in.
+template <int N, bool kWatch = false, typename Addr, typename Use, typename Skip, typename Hook, typename Hook2>
+__device__ __forceinline__ void poll_tagged(Addr addr, int n, uint32_t tag, Use use, Skip skip, Hook after_first,
+                                            Hook2 on_first_in) {
+  const int tid = threadIdx.x;
+  uint32_t todo = 0, pay[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    pay[j] = 0;
+    if (tid + 256 * j < n && !skip(tid + 256 * j)) todo |= 1u << j;
   }
-  __syncthreads();
-  const uint32_t lo = (uint32_t)tk;
-  if (lo == 0xffffffffu) return nullptr;
-  return pool + (uint64_t)(lo - 1) * 256;
+  const uint32_t want = todo;
+  bool watching = kWatch;
+  for (int it = 0;; ++it) {
+    uint64_t v[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = ((todo >> j) & 1u) ? get_tag(addr(tid + 256 * j)) : 0ull;
+    if (it == 0) after_first();
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (((todo >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
+        pay[j] = (uint32_t)v[j];
+        todo &= ~(1u << j);
+      }
+    if (kWatch && watching && __syncthreads_or(todo != want)) {
+      on_first_in();
+      watching = false;
+    }
+    if (!__syncthreads_or(todo != 0u)) break;
+    if (it >= kSpinLimit) {
+      if (tid == 0) flag_device_error(4u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    if ((want >> j) & 1u) use(tid + 256 * j, pay[j]);
+}
+template <int N, typename Addr, typename Use, typename Skip, typename Hook>
+__device__ __forceinline__ void poll_tagged(Addr addr, int n, uint32_t tag, Use use, Skip skip, Hook after_first) {
+  poll_tagged<N, false>(addr, n, tag, use, skip, after_first, [] {});
+}
+template <int N, typename Addr, typename Use>
+__device__ __forceinline__ void poll_tagged(Addr addr, int n, uint32_t tag, Use use) {
+  poll_tagged<N, false>(addr, n, tag, use, [](int) { return false; }, [] {}, [] {});
 }
 
-struct FusedArgs {
-  DecodeArgs A;              // weights, shapes, partial buffers, outputs
-  const uint8_t* router_blob;
-  const float* offset;       // [E] or null
-  double* rt_partial;        // [nsplit_r][E]
-  int32_t* idx_out;          // [top_k] caller's picks
-  float* w_out;              // [top_k] caller's weights
-  uint32_t* sync;            // kFusedSyncWords
-  int n_experts, nsplit_r;
-  int n_rt, n_sg, n_rg, n_sd, n_rd;
-};
+__device__ __forceinline__ uint32_t read_epoch(const FusedArgs& F) {
+  return ld_agent_u(&F.sync[(blockIdx.x % kEpochCopies) * kSyncLine]);
+}
+// Thread 0: this workgroup has read the epoch (the inline asm makes the increment wait
+// for the value read). No result is returned, so nothing waits for the atomic itself.
+__device__ __forceinline__ void arrive_epoch(const FusedArgs& F, uint32_t epoch) {
+  uint32_t one = 1u;
+  asm volatile("" : "+v"(one) : "v"(epoch));
+  __hip_atomic_fetch_add(&F.sync[(kEpochCopies + blockIdx.x % kArrivalCounters) * kSyncLine], one,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The last workgroup of the grid: waits for the arrivals of all others (blocks
+// b < gridDim.x - 1 arrive at counter b % kArrivalCounters), then clears the counters
+// and writes epoch + 1 into every copy.
+__device__ __forceinline__ void epoch_keeper(const FusedArgs& F, uint32_t epoch) {
+  const int tid = threadIdx.x;
+  const int n = (int)gridDim.x - 1;
+  if (tid < kArrivalCounters) {
+    const uint32_t expect = n > tid ? (uint32_t)((n - 1 - tid) / kArrivalCounters + 1) : 0u;
+    const uint32_t* c = &F.sync[(kEpochCopies + tid) * kSyncLine];
+    for (int it = 0; ld_agent_u(c) < expect; ++it) {
+      if (it > kSpinLimit) {
+        flag_device_error(4u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+  if (tid < kArrivalCounters) st_agent_u(&F.sync[(kEpochCopies + tid) * kSyncLine], 0u);
+  if (tid < kEpochCopies) st_agent_u(&F.sync[tid * kSyncLine], epoch + 1u);
+}
 
-// group_dot with the vector operand in LDS as 32 hi and 32 lo pairs (hh, hl point at
-// the group's pair 0): the pairs are read in two batches of 16, one LDS wait each,
-// and accumulated in the same order as group_dot, so the result is the same
+// x into LDS. kRaw (router): bf16 x as stored pairs, fp32 x as values. Otherwise
+// (gate/up): bf16 pairs, or for fp32 x hi pairs at xb[0, d/2) and lo pairs at
+// xb[kFusedXWords/2, ...) with hi + lo the fp32 value to 16 significant bits;
+// then xg = sums over the 32-column halves of each group. Ends with a barrier.
+template <typename XT, bool kRaw>
+__device__ __forceinline__ void stage_x(const XT* __restrict__ x, int d, FusedSmem& S) {
+  const int tid = threadIdx.x;
+  if constexpr (sizeof(XT) == 2 || kRaw) {
+    for (int i = tid; i < d * (int)sizeof(XT) / 16; i += 256)
+      *reinterpret_cast<uint4*>(&S.xb[4 * i]) = ldg16(reinterpret_cast<const uint8_t*>(x) + 16 * i);
+  } else {
+    for (int i = tid; i < d / 4; i += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(x + 4 * i);
+      const float xv[4] = {v.x, v.y, v.z, v.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        hi[c] = f32_to_bf16_bits(xv[c]);
+        lo[c] = f32_to_bf16_bits(xv[c] - bf16_to_f32((uint16_t)hi[c]));
+      }
+      S.xb[2 * i] = hi[0] | (hi[1] << 16);
+      S.xb[2 * i + 1] = hi[2] | (hi[3] << 16);
+      S.xb[kFusedXWords / 2 + 2 * i] = lo[0] | (lo[1] << 16);
+      S.xb[kFusedXWords / 2 + 2 * i + 1] = lo[2] | (lo[3] << 16);
+    }
+  }
+  __syncthreads();
+  if constexpr (!kRaw) {
+    if (tid < 2 * (d / kGroup)) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const uint32_t w = S.xb[16 * tid + p];
+        sum += bf16_lo(w) + bf16_hi(w);
+        if constexpr (sizeof(XT) == 4) {
+          const uint32_t l = S.xb[kFusedXWords / 2 + 16 * tid + p];
+          sum += bf16_lo(l) + bf16_hi(l);
+        }
+      }
+      S.xg[tid] = sum;
+    }
+    __syncthreads();
+  }
+}
+
+// Reads the logits (this block's copy) and ranks the experts: S.lg = logits,
+// S.sel_e[0, top_k) = the picks in rank order (logit desc, id asc; NaN as -inf).
+// The ranks are counted on unique 31-bit keys: the top 31 - b bits of the order key
+// above b bits of (E - 1 - id), b = 7 for E <= 128, else 8, so ties go to the lower
+// id. A key beats another when their difference is negative: a subtraction and a
+// shift, independent of each other and summed in four chains (no compare-and-carry
+// chain). That is the true order wherever the truncated parts differ; when two
+// neighbours among ranks 0..top_k share theirs, the ranking is redone on the whole
+// keys (rank_topk). Ends with a barrier.
+__device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
+  const int tid = threadIdx.x, E = F.E, k = F.top_k;
+  const uint64_t* lg = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride;
+  poll_tagged<2>([&](int i) { return lg + i; }, 2 * E, tag, [&](int i, uint32_t p) { S.lgw[i] = p; });
+  __syncthreads();
+  const int idbits = E <= 128 ? 7 : 8;
+  if (tid < E) {
+    const double v = __hiloint2double((int)S.lgw[2 * tid + 1], (int)S.lgw[2 * tid]);
+    const uint64_t key = order_key(v);
+    S.lg[tid] = v;
+    S.key[tid] = key;
+    S.kp[tid] = ((uint32_t)(key >> (33 + idbits)) << idbits) | (uint32_t)(E - 1 - tid);
+  }
+  __syncthreads();
+  // thread t: expert t % E against the competitors of share t / E (256 / E shares)
+  const int parts = E == 64 ? 4 : E == 128 ? 2 : 1;
+  const int per = E / parts, h = tid / E, me = tid % E;
+  const int mine = (int)S.kp[me];
+  int r4[4] = {0, 0, 0, 0};
+  if (h < parts) {
+    for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
+      u32x4_t kk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kk[i] = *reinterpret_cast<const u32x4_t*>(&S.kp[c0 + 4 * i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r4[c] += (int)((uint32_t)(mine - (int)kk[i][c]) >> 31);
+    }
+    S.rank[h][me] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+  }
+  __syncthreads();
+  if (tid < E) {
+    int rk = 0;
+    for (int j = 0; j < parts; ++j) rk += S.rank[j][tid];
+    if (rk <= k) S.sel_e[rk] = tid;  // ranks 0..top_k (sel_e holds 17)
+  }
+  __syncthreads();
+  const bool clash = tid < min(k, E - 1) && (S.kp[S.sel_e[tid]] >> idbits) == (S.kp[S.sel_e[tid + 1]] >> idbits);
+  if (__syncthreads_or(clash)) rank_topk(S.key, E, k, S.rank, S.sel_e);
+}
+
+// The blob of the expert picked for `slot` (nullptr and the error flag if its table
+// entry is outside the pool). slot_entry: thread t < E holds slot_table[t].
+__device__ __forceinline__ const uint8_t* routed_blob(const FusedArgs& F, int slot, uint32_t tag,
+                                                      uint32_t slot_entry, FusedSmem& S) {
+  if (threadIdx.x < F.E) S.slots[threadIdx.x] = slot_entry;
+  rank_logits(F, tag, S);
+  const uint32_t b = S.slots[S.sel_e[slot]];  // ranks are a permutation: sel_e is a valid id
+  if ((uint64_t)b >= F.n_blobs) {
+    if (threadIdx.x == 0) flag_device_error(1u);
+    return nullptr;
+  }
+  return F.pool + (uint64_t)b * F.stride;
+}
+
+// ------------------------------------------------------------------ router item
+
+template <typename XT>
+__device__ __forceinline__ float x_at(const FusedSmem& S, int col) {
+  if constexpr (sizeof(XT) == 2) return bf16_to_f32((uint16_t)(S.xb[col >> 1] >> (16 * (col & 1))));
+  else return __uint_as_float(S.xb[col]);
+}
+
+// experts [2 item, +2): thread t takes row (t & 1), column quarter (t >> 1) & 3 and the
+// groups (t >> 3) + 32 j; products w * x are exact in fp64 (w = s q + b has at most
+// 20 significant bits, x at most 24) and the sums are fp64.
+template <typename XT>
+__device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __restrict__ x, int item, uint32_t tag,
+                                             uint32_t epoch, FusedSmem& S) {
+  const int tid = threadIdx.x;
+  const int G = F.d / kGroup;
+  const int e0 = item * kFusedRouterE, nb = e0 / 64, row = e0 % 64 + (tid & 1);
+  const int c = (tid >> 1) & 3, gs = tid >> 3;
+  constexpr int J = kFusedMaxG / 32 + 1;
+  u32x4_t q[J];
+  uint32_t sb[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int g = min(gs + 32 * j, G - 1);
+    const uint8_t* t = F.router_blob + ((uint64_t)nb * G + g) * kTile8;
+    q[j] = *reinterpret_cast<const u32x4_t*>(t + c * 1024 + row * 16);
+    sb[j] = ldg4(t + kTile8Codes + row * 4);
+  }
+  if (tid == 0) arrive_epoch(F, epoch);  // before the first wait, which covers it
+  stage_x<XT, true>(x, F.d, S);
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int g = gs + 32 * j;
+    if (g < G) {
+      const double s = (double)bf16_lo(sb[j]), b = (double)bf16_hi(sb[j]);
+      const int col = g * kGroup + 16 * c;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const double w = fma(s, (double)((q[j][m >> 2] >> (8 * (m & 3))) & 0xffu), b);
+        acc = fma(w, (double)x_at<XT>(S, col + m), acc);
+      }
+    }
+  }
+  S.rd[tid] = acc;
+  __syncthreads();
+  if (tid < kFusedRouterE) {
+    double l = 0.0;
+    for (int k = 0; k < 128; ++k) l += S.rd[tid + 2 * k];
+    if (F.offset) l += (double)F.offset[e0 + tid];
+    S.lgv[tid] = l;
+  }
+  __syncthreads();
+  // 2 words per expert into every copy: thread t stores word t % 4 of copy t / 4
+  if (tid < 2 * kFusedRouterE * kLgCopies) {
+    const int wd = tid % (2 * kFusedRouterE), copy = tid / (2 * kFusedRouterE);
+    const uint64_t bits = (uint64_t)__double_as_longlong(S.lgv[wd >> 1]);
+    put_tag(&F.lg_tag[(size_t)copy * kLgStride + 2 * e0 + wd], (uint32_t)(bits >> (32 * (wd & 1))), tag);
+  }
+}
+
+// ------------------------------------------------------------------ gate/up item
+
+// sum over 32 columns of one row: codes q (4 words, see common.h) against 16 x pairs
+// (and 16 lo pairs for fp32 x)
+template <bool kLo>
+__device__ __forceinline__ float half_dot(const u32x4_t& q, const uint32_t* xp, const uint32_t* xl) {
+  u32x4_t xv[4], lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xv[i] = *reinterpret_cast<const u32x4_t*>(xp + 4 * i);
+    if constexpr (kLo) lv[i] = *reinterpret_cast<const u32x4_t*>(xl + 4 * i);
+  }
+  float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const NibK nk;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t p = nk.pair(q[jj], t);
+      a4[t] = dot2(p, xv[jj][t], a4[t]);
+      if constexpr (kLo) a4[t] = dot2(p, lv[jj][t], a4[t]);
+    }
+  return (a4[0] + a4[1]) + (a4[2] + a4[3]);
+}
+
+// Rows [16 q4, +16) of 64-row block nb of the gate and up matrices, whole reduction.
+// Lane l of wave w: group pair (w + 4 i), group 2 (w + 4 i) + (l >> 5), column half
+// (l >> 4) & 1, row l & 15: each wavefront load is 4 runs of 256 contiguous bytes.
+template <typename XT>
+__device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __restrict__ x, int u, bool routed,
+                                             uint32_t tag, uint32_t epoch, FusedSmem& S) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = F.d / kGroup;
+  int slot = F.top_k, Fd = F.fs;
+  if (routed) {
+    const int per = F.f / kFusedRows;
+    slot = u / per;
+    u -= slot * per;
+    Fd = F.f;
+  }
+  const int nb = u >> 2, q4 = u & 3;
+  const int tp = lane >> 5, half = (lane >> 4) & 1, row = q4 * kFusedRows + (lane & 15);
+  u32x4_t q[2][kFusedGuI];
+  uint32_t sb[2][kFusedGuI];
+  auto load = [&](const uint8_t* blob) {
+    const uint64_t mbytes = m4_bytes(Fd, F.d);
+#pragma unroll
+    for (int i = 0; i < kFusedGuI; ++i)
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        const int g = min(2 * (wave + 4 * i) + tp, G - 1);
+        const uint8_t* t = blob + mat * mbytes + ((uint64_t)nb * G + g) * kTile4;
+        q[mat][i] = *reinterpret_cast<const u32x4_t*>(t + half * 1024 + row * 16);
+        sb[mat][i] = ldg4(t + kTile4Codes + row * 4);
+      }
+  };
+  // the shared expert's weights stream from the start; a routed expert's once it is known
+  const uint8_t* blob = F.shared_blob;
+  if (!routed) {
+    load(blob);
+    if (tid == 0) arrive_epoch(F, epoch);
+  }
+  const uint32_t slot_entry = (routed && tid < F.E) ? F.slot_table[tid] : 0u;
+  stage_x<XT, false>(x, F.d, S);
+  if (routed) {
+    // the arrival goes after the weight loads: no wait on the ticket's path covers it
+    blob = routed_blob(F, slot, tag, slot_entry, S);
+    if (blob) load(blob);
+    if (tid == 0) arrive_epoch(F, epoch);
+  }
+  float acc[2] = {0.0f, 0.0f};
+  if (blob) {
+#pragma unroll
+    for (int i = 0; i < kFusedGuI; ++i) {
+      const int g = 2 * (wave + 4 * i) + tp;
+      if (2 * (wave + 4 * i) < G) {  // wave-uniform; lanes of a missing odd group add nothing
+        const int gc = min(g, G - 1);
+        const uint32_t* xp = S.xb + gc * 32 + half * 16;
+        const float xs = S.xg[2 * gc + half];
+#pragma unroll
+        for (int mat = 0; mat < 2; ++mat) {
+          const float a = half_dot<sizeof(XT) == 4>(q[mat][i], xp, xp + kFusedXWords / 2);
+          const float s = bf16_lo(sb[mat][i]), b = bf16_hi(sb[mat][i]);
+          const float v = fmaf(s, a, fmaf(-128.0f, s, b) * xs);
+          acc[mat] += g < G ? v : 0.0f;
+        }
+      }
+    }
+  }
+  S.red[0][wave][lane] = acc[0];
+  S.red[1][wave][lane] = acc[1];
+  __syncthreads();
+  if (tid < 2 * kFusedRows) {
+    const int mat = tid >> 4, r = tid & 15;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) v += S.red[mat][w][r + 16 * k4];
+    S.gu[mat][r] = v;
+  }
+  __syncthreads();
+  if (tid < kFusedRows) S.hv[tid] = gelu_tanh(S.gu[0][tid]) * S.gu[1][tid];
+  __syncthreads();
+  if (tid < kFusedRows * kHCopies) {
+    const int r = tid % kFusedRows, copy = tid / kFusedRows;
+    put_tag(&F.h_tag[copy * F.h_stride + (size_t)slot * F.fmax + nb * 64 + q4 * kFusedRows + r],
+            __float_as_uint(S.hv[r]), tag);
+  }
+}
+
+// ------------------------------------------------------------------ down item (+ combine)
+
+// group sum of one row against h in LDS as 32 hi and 32 lo pairs (hh, hl point at the
+// group's pair 0), read in two batches of 16 pairs (one LDS wait each)
 __device__ __forceinline__ float group_dot_lds(const uint32_t* hh, const uint32_t* hl, uint4 qa, uint4 qb,
                                                uint32_t sbw, float Vg) {
   const uint32_t words[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
   float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const NibK nk;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     uint4 h4[4], l4[4];
@@ -152,7 +509,7 @@ __device__ __forceinline__ float group_dot_lds(const uint32_t* hh, const uint32_
       const uint32_t lv[4] = {l4[jj].x, l4[jj].y, l4[jj].z, l4[jj].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint32_t p = nib_pair(w, t);
+        const uint32_t p = nk.pair(w, t);
         acc4[t] = dot2(p, hv[t], acc4[t]);
         acc4[t] = dot2(p, lv[t], acc4[t]);
       }
@@ -163,7 +520,7 @@ __device__ __forceinline__ float group_dot_lds(const uint32_t* hh, const uint32_
   return fmaf(s, a, fmaf(-128.0f, s, b) * Vg);
 }
 
-// weights of one 64-row block for groups g0 + wave + 4i (i < GW), loaded ahead of use
+// weights of one 64-row block for groups g0 + wave + 4i (i < GW) of [g0, g1), loaded ahead of use
 template <int GW>
 struct RowLoads {
   uint4 qa[GW], qb[GW];
@@ -180,360 +537,167 @@ struct RowLoads {
       }
     }
   }
-  // against h in LDS: pairs of group g at hh/hl + (g - g0) * 32, group sums at gs[g - g0]
+  // against h in LDS: pairs of group g at hh/hl + g * 32, group sums at gs[g]
   __device__ __forceinline__ float dot_lds(int g0, int g1, int wave, const uint32_t* hh, const uint32_t* hl,
                                            const float* gs) const {
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
       const int g = g0 + wave + 4 * i;
-      if (g < g1) acc += group_dot_lds(hh + (g - g0) * 32, hl + (g - g0) * 32, qa[i], qb[i], sb[i], gs[g - g0]);
+      if (g < g1) acc += group_dot_lds(hh + g * 32, hl + g * 32, qa[i], qb[i], sb[i], gs[g]);
     }
     return acc;
   }
 };
 
-struct FusedSmem {
-  double xs[256];
-  double red[4][64];
-  double lg[256];
-  double sel_v[16];
-  int sel_e[16];
-  int rank[4][256];
-  float redf[4][64];
-  uint32_t slots[256];   // the layer's slot table (last router workgroup)
-  __attribute__((aligned(16))) uint32_t hh[12 * 32];  // h hi pairs for up to 12 groups
-  __attribute__((aligned(16))) uint32_t hl[12 * 32];
-  float hsum[12];
-  int last;
-};
-
-// ------------------------------------------------------------------ router item
-
-template <typename XT>
-__device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __restrict__ x, int item, FusedSmem& S) {
-  const DecodeArgs& A = F.A;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int E = F.n_experts, nbe = E / 64;
-  const int nb = item % nbe, split = item / nbe;
-  const int G = A.d / kGroup;
-  const int g = split * 4 + wave;
-  uint4 q[4];
-  uint32_t sbw = 0;
-  if (g < G) {
-    const uint8_t* tile = F.router_blob + ((size_t)nb * G + g) * kTile8;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) q[c] = ldg16(tile + c * 1024 + lane * 16);
-    sbw = ldg4(tile + kTile8Codes + lane * 4);
-  }
-  const int xi = split * 256 + tid;
-  S.xs[tid] = xi < A.d ? (double)x_as_f32(x[xi]) : 0.0;
+// Values [j0, j1) of one slot's h (j0, j1 multiples of 64) from their tagged words into
+// LDS at the same positions, as hi and lo bf16 halves (hi pairs at xb, lo pairs at
+// xb + kFusedXWords/2), with the per-group sums of hi + lo.
+// on_first_in() (kWatch) runs once, as soon as the first values are in.
+template <bool kWatch = false, typename Hook = void (*)()>
+__device__ __forceinline__ void gather_h(const uint64_t* src, int j0, int j1, uint32_t tag, FusedSmem& S,
+                                         Hook on_first_in = nullptr) {
+  uint16_t* hh = reinterpret_cast<uint16_t*>(S.xb);
+  uint16_t* hl = reinterpret_cast<uint16_t*>(S.xb + kFusedXWords / 2);
+  for (int base = j0; base < j1; base += 1024)
+    poll_tagged<4, kWatch>(
+        [&](int i) { return src + base + i; }, min(1024, j1 - base), tag,
+        [&](int i, uint32_t p) {
+          const float h = __uint_as_float(p);
+          const uint32_t hi = f32_to_bf16_bits(h);
+          hh[base + i] = (uint16_t)hi;
+          hl[base + i] = (uint16_t)f32_to_bf16_bits(h - bf16_to_f32((uint16_t)hi));
+        },
+        [](int) { return false; }, [] {},
+        [&] {
+          if constexpr (kWatch) on_first_in();
+        });
   __syncthreads();
-  double acc = 0.0;
-  if (g < G) {
-    const double s = (double)bf16_lo(sbw), b = (double)bf16_hi(sbw);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t words[4] = {q[c].x, q[c].y, q[c].z, q[c].w};
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        acc = fma(fma(s, (double)((words[j >> 2] >> (8 * (j & 3))) & 0xffu), b), S.xs[wave * 64 + c * 16 + j], acc);
-    }
-  }
-  S.red[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    st_agent_d(&F.rt_partial[(size_t)split * E + nb * 64 + lane],
-               ((S.red[0][lane] + S.red[1][lane]) + S.red[2][lane]) + S.red[3][lane]);
-    wait_mem();
-    if (lane == 0) S.last = (arrive(&F.sync[FusedSync::kRouter]) == (uint32_t)(F.n_rt - 1));
-  }
-  __syncthreads();
-  if (!S.last) return;
-  // last router workgroup: the slot table (read while the partials arrive), the full
-  // logits (tpe threads per expert, loads in flight together), the ranking, the tickets
-  const uint32_t slot_entry = tid < E ? A.slot_table[tid] : 0u;
-  const int tpe = 256 / E;
-  const int e = tid % E, sub = tid / E;
-  double part = 0.0;
-  for (int sp0 = sub; sp0 < F.nsplit_r; sp0 += 8 * tpe) {
-    double pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int sp = sp0 + i * tpe;
-      pv[i] = sp < F.nsplit_r ? ld_agent_d(&F.rt_partial[(size_t)sp * E + e]) : 0.0;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part += pv[i];
-  }
-  S.xs[tid] = part;  // xs is free now: per-(sub, expert) partial sums
-  __syncthreads();
-  if (tid < E) {
-    double l = 0.0;
-    for (int s2 = 0; s2 < tpe; ++s2) l += S.xs[s2 * E + tid];
-    if (F.offset) l += (double)F.offset[tid];
-    S.lg[tid] = l;
-  }
-  __syncthreads();
-  // the ranking (rank_topk: integer order keys, ties by id) and the picks' logits
-  uint64_t* key = reinterpret_cast<uint64_t*>(S.xs);  // xs is free now
-  if (tid < E) {
-    key[tid] = order_key(S.lg[tid]);
-    S.slots[tid] = slot_entry;
-  }
-  __syncthreads();
-  rank_topk(key, E, A.top_k, S.rank, S.sel_e);
-  if (tid < A.top_k) S.sel_v[tid] = S.lg[S.sel_e[tid]];
-  __syncthreads();
-  if (wave == 0) {
-    const int k = A.top_k;
-    const double ex = lane < k ? exp(S.sel_v[lane] - S.sel_v[0]) : 0.0;
-    double sum = 0.0;
-    for (int t = 0; t < k; ++t) sum += __shfl(ex, t, 64);
-    // ticket of slot (lane & 15), stored by 4 lanes into 4 of the 16 record copies each
-    const int t = lane & 15;
-    const double ext = __shfl(ex, t, 64);
-    uint64_t ticket = 0;
-    if (t < k) {
-      const int ei = S.sel_e[t];
-      const float wv = (float)(ext / sum);
-      const uint8_t* blob = nullptr;  // as expert_blob, from the table read above
-      if (ei < 0 || ei >= E) {
-        flag_device_error(2u);
-      } else if ((uint64_t)S.slots[ei] >= A.n_blobs) {
-        flag_device_error(1u);
-      } else {
-        blob = A.pool + (uint64_t)S.slots[ei] * A.stride;
-      }
-      const uint32_t lo = blob ? (uint32_t)((uint64_t)(blob - A.pool) / 256 + 1) : 0xffffffffu;
-      ticket = ((uint64_t)__float_as_uint(wv) << 32) | lo;
-      if (lane < 16) {
-        F.idx_out[t] = ei;
-        F.w_out[t] = wv;
-      }
-      for (int c = lane >> 4; c < FusedSync::kCopies; c += 4)
-        __hip_atomic_store(reinterpret_cast<uint64_t*>(F.sync + FusedSync::rec(c)) + t, ticket, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ gate/up item
-
-template <typename XT>
-__device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __restrict__ x, int u, bool routed,
-                                             FusedSmem& S) {
-  const DecodeArgs& A = F.A;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int slot, Fd;
-  const uint8_t* blob;
-  if (routed) {
-    const int per = 2 * (A.f / 64) * A.P;
-    slot = u / per;
-    u -= slot * per;
-    Fd = A.f;
-    blob = wait_ticket(A.pool, F.sync, slot);
-  } else {
-    slot = A.top_k;
-    Fd = A.fs;
-    blob = A.shared_blob;
-  }
-  const int NB = Fd / 64;
-  const int mat = u / (NB * A.P);
-  const int nb = (u / A.P) % NB;
-  const int part = u % A.P;
-  const int G = A.d / kGroup;
-  const int GP = (G + A.P - 1) / A.P;
-  const int g0 = part * GP, g1 = min(G, g0 + GP);
-  float acc = 0.0f;
-  if (blob) {
-    const uint8_t* rowblock = blob + (uint64_t)mat * m4_bytes(Fd, A.d) + (uint64_t)nb * G * kTile4;
-    if constexpr (sizeof(XT) == 2)
-      acc = block_rows_dot<3>(rowblock, g0, g1, wave, lane, VecBF16{reinterpret_cast<const uint32_t*>(x)},
-                              XGroupSum<XT>{x});
-    else
-      acc = block_rows_dot<3>(rowblock, g0, g1, wave, lane, VecF32{reinterpret_cast<const float*>(x)},
-                              XGroupSum<XT>{x});
-  }
-  const float r = reduce_waves4(acc, S.redf, wave, lane);
-  if (wave == 0) {
-    const size_t pbase = ((size_t)(slot * 2 + mat) * A.nbmax + nb) * A.P;
-    st_agent(&A.gu_partial[(pbase + part) * 64 + lane], r);
-    wait_mem();
-    if (lane == 0) {
-      // level 1: the 2P items of this (slot, block); level 2: the blocks of the slot
-      uint32_t* l1 = &F.sync[FusedSync::kL1 + slot * A.nbmax + nb];
-      if (arrive(l1) == (uint32_t)(2 * A.P - 1)) {
-        st_agent_u(l1, 0u);
-        const int c2 = routed ? FusedSync::kSlot0 + slot : FusedSync::kShared;
-        if (arrive(&F.sync[c2]) == (uint32_t)(NB - 1)) raise_flag(F.sync, routed ? 2 + slot : 1);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ down item (+ combine)
-
-// h = gelu(sum of gate parts) * (sum of up parts) for d_ff groups [g0, g1) of `slot`
-// (at most 12 groups, P <= 4), into LDS as hi/lo bf16 pairs with per-group sums
-__device__ __forceinline__ void build_h(const DecodeArgs& A, int slot, int g0, int g1, FusedSmem& S) {
-  const int tid = threadIdx.x;
-  const int n = (g1 - g0) * 64;
-  float gv[3][4], uv[3][4];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int idx = tid + 256 * i;
-    const int j = g0 * 64 + idx, nbj = j >> 6, r = j & 63;
-    const size_t gb = ((size_t)(slot * 2 + 0) * A.nbmax + nbj) * A.P;
-    const size_t ub = ((size_t)(slot * 2 + 1) * A.nbmax + nbj) * A.P;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const bool ok = idx < n && p < A.P;
-      gv[i][p] = ok ? ld_agent(&A.gu_partial[(gb + p) * 64 + r]) : 0.0f;
-      uv[i][p] = ok ? ld_agent(&A.gu_partial[(ub + p) * 64 + r]) : 0.0f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int idx = tid + 256 * i;
-    if (idx < n) {
-      const float gs = ((gv[i][0] + gv[i][1]) + gv[i][2]) + gv[i][3];
-      const float us = ((uv[i][0] + uv[i][1]) + uv[i][2]) + uv[i][3];
-      const float h = gelu_tanh(gs) * us;
-      const uint32_t hi = f32_to_bf16_bits(h);
-      const uint32_t lo = f32_to_bf16_bits(h - bf16_to_f32((uint16_t)hi));
-      reinterpret_cast<uint16_t*>(S.hh)[idx] = (uint16_t)hi;
-      reinterpret_cast<uint16_t*>(S.hl)[idx] = (uint16_t)lo;
-    }
-  }
-  __syncthreads();
-  // group sums of hi + lo, one wave per group
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int gi = wave; gi < g1 - g0; gi += 4) {
-    const int i = gi * 64 + lane;
-    const float v = bf16_to_f32(reinterpret_cast<const uint16_t*>(S.hh)[i]) +
-                    bf16_to_f32(reinterpret_cast<const uint16_t*>(S.hl)[i]);
-    const float s = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int gi = j0 / kGroup + wave; gi < j1 / kGroup; gi += 4) {
+    const int i = gi * kGroup + lane;
+    const float s = wave_sum(bf16_to_f32(hh[i]) + bf16_to_f32(hl[i]));
     if (lane == 0) S.hsum[gi] = s;
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ void fused_combine(const FusedArgs& F, int nb) {
-  const DecodeArgs& A = F.A;
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x >= 64) return;
-  const int n = nb * 64 + lane;
-  const uint64_t* rec = my_record(F.sync);
-  float sp[4], ev[16], wv[16];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) sp[p] = p < A.Ps ? ld_agent(&A.shared_part[(size_t)p * A.d + n]) : 0.0f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    ev[k] = k < A.top_k ? ld_agent(&A.expert_out[(size_t)k * A.d + n]) : 0.0f;
-    wv[k] = k < A.top_k ? __uint_as_float((uint32_t)(ld_agent_u64(&rec[k]) >> 32)) : 0.0f;
-  }
-  float yv = ((sp[0] + sp[1]) + sp[2]) + sp[3];
-#pragma unroll
-  for (int k = 0; k < 16; ++k)
-    if (k < A.top_k) yv = fmaf(wv[k], ev[k], yv);
-  A.y[n] = yv;
-  if (A.residual) A.residual[n] = (uint16_t)f32_to_bf16_bits(bf16_to_f32(A.residual[n]) + yv);
-  const int nbd = A.d / 64;
-  bool final = false;
-  if (lane == 0) {
-    st_agent_u(&F.sync[FusedSync::combine(A.top_k, nb)], 0u);
-    final = arrive(&F.sync[FusedSync::done(A.top_k, nbd)]) == (uint32_t)(nbd - 1);
-  }
-  if (__shfl(final ? 1 : 0, 0, 64)) {
-    // every item has finished waiting: reset counters, flags and tickets for the next call,
-    // spread over the wave's lanes
-    if (lane < FusedSync::kSlot0 + A.top_k) st_agent_u(&F.sync[lane], 0u);
-    if (lane == 0) st_agent_u(&F.sync[FusedSync::done(A.top_k, nbd)], 0u);
-    for (int i = lane; i < (1 + A.top_k) * FusedSync::kCopies; i += 64)
-      st_agent_u(&F.sync[FusedSync::flag(1 + i / FusedSync::kCopies, i % FusedSync::kCopies)], 0u);
-    for (int i = lane; i < A.top_k * FusedSync::kCopies; i += 64)
-      __hip_atomic_store(reinterpret_cast<uint64_t*>(F.sync + FusedSync::rec(i / A.top_k)) + i % A.top_k,
-                         (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The picks and their softmax weights into S.sel_e, S.selw (fp64 softmax over the
+// picked logits, fixed summation order).
+__device__ __forceinline__ void pick_weights(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
+  const int tid = threadIdx.x, lane = tid & 63, k = F.top_k;
+  rank_logits(F, tag, S);
+  if (tid < 64) {
+    const double ex = lane < k ? exp(S.lg[S.sel_e[lane]] - S.lg[S.sel_e[0]]) : 0.0;
+    double sum = 0.0;
+    for (int t = 0; t < k; ++t) sum += __shfl(ex, t, 64);
+    if (lane < k) S.selw[lane] = (float)(ex / sum);
   }
 }
 
-__device__ __forceinline__ void fused_down(const FusedArgs& F, int u, bool routed, FusedSmem& S) {
-  const DecodeArgs& A = F.A;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int NBd = A.d / 64;
-  int slot, Fd, g0, g1, part = 0, nb;
-  const uint8_t* blob;
-  if (routed) {
-    slot = u / NBd;
-    nb = u % NBd;
-    Fd = A.f;
-    g0 = 0;
-    g1 = Fd / kGroup;
-    blob = wait_ticket(A.pool, F.sync, slot);
-  } else {
-    slot = A.top_k;
-    nb = u / A.Ps;
-    part = u % A.Ps;
-    Fd = A.fs;
-    const int G = Fd / kGroup, GP = (G + A.Ps - 1) / A.Ps;
-    g0 = part * GP;
-    g1 = min(G, g0 + GP);
-    blob = A.shared_blob;
-  }
-  const uint8_t* rowblock = blob ? blob + 2 * m4_bytes(Fd, A.d) + (uint64_t)nb * (Fd / kGroup) * kTile4 : nullptr;
-  RowLoads<3> w;
-  if (rowblock) w.load(rowblock, g0, g1, wave, lane);  // weights stream while h is produced
-  wait_flag(F.sync, routed ? 2 + slot : 1);
-  build_h(A, slot, g0, g1, S);
-  float acc = 0.0f;
-  if (rowblock)
-    acc = w.dot_lds(g0, g1, wave, S.hh, S.hl, S.hsum);
-  const float r = reduce_waves4(acc, S.redf, wave, lane);
-  if (wave == 0) {
-    const int n = nb * 64 + lane;
-    st_agent(routed ? &A.expert_out[(size_t)slot * A.d + n] : &A.shared_part[(size_t)part * A.d + n], r);
-    wait_mem();
-    if (lane == 0)
-      S.last = (arrive(&F.sync[FusedSync::combine(A.top_k, nb)]) == (uint32_t)(A.top_k + A.Ps - 1));
-  }
+// y for rows [64 ob, +64) once the picks are known (pick_weights): r (wave 0) is the
+// shared expert's first half for the row; adds its second half, then the routed
+// outputs weighted by the softmax over the picks, in pick order.
+__device__ __forceinline__ void fused_combine(const FusedArgs& F, int ob, float r, uint32_t tag, FusedSmem& S) {
+  const int tid = threadIdx.x, lane = tid & 63, k = F.top_k;
+  poll_tagged<5>([&](int i) { return F.eo_tag + (size_t)(i >> 6) * F.d + ob * 64 + (i & 63); }, 64 * (k + 1), tag,
+                 [&](int i, uint32_t p) { S.eo[i >> 6][i & 63] = __uint_as_float(p); });
   __syncthreads();
-  if (S.last) fused_combine(F, nb);
+  if (tid < 64) {
+    float yv = r + S.eo[k][lane];
+    for (int s = 0; s < k; ++s) yv = fmaf(S.selw[s], S.eo[s][lane], yv);
+    const int n = ob * 64 + lane;
+    F.y[n] = yv;
+    if (F.residual) F.residual[n] = (uint16_t)f32_to_bf16_bits(bf16_to_f32(F.residual[n]) + yv);
+    if (ob == 0 && lane < k) {
+      F.idx_out[lane] = S.sel_e[lane];
+      F.w_out[lane] = S.selw[lane];
+    }
+  }
+}
+
+// Output rows [64 ob, +64) of the down matrix of `slot`, over groups [g0, g1) of its h.
+// kind 0: routed slot u / (d/64) over its whole h -> expert_out and its tagged copy;
+// kind 1: the shared expert's second half -> tagged partial; kind 2: the shared
+// expert's first half, then the combine of the rows. The weights stream as soon as
+// the expert is known, while h is still being produced.
+template <int GW>
+__device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, uint32_t tag, uint32_t epoch,
+                                           FusedSmem& S) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NBd = F.d / 64;
+  int slot = F.top_k, ob = u, Fd = F.fs;
+  if (kind == 0) {
+    slot = u / NBd;
+    ob = u % NBd;
+    Fd = F.f;
+  }
+  const int Gin = Fd / kGroup, Gh = (Gin + 1) / 2;
+  const int g0 = kind == 1 ? Gh : 0, g1 = kind == 2 ? Gh : Gin;
+  const uint32_t slot_entry = (kind == 0 && tid < F.E) ? F.slot_table[tid] : 0u;
+  const uint8_t* blob = kind == 0 ? routed_blob(F, slot, tag, slot_entry, S) : F.shared_blob;
+  RowLoads<GW> w;
+  const uint8_t* rowblock = blob ? blob + 2 * m4_bytes(Fd, F.d) + (uint64_t)ob * Gin * kTile4 : nullptr;
+  const uint64_t* hsrc = F.h_tag + (blockIdx.x % kHCopies) * F.h_stride + (size_t)slot * F.fmax;
+  if (kind == 0) {
+    // a routed expert's down weights wait until its h starts to come in, so that they do
+    // not take memory bandwidth from the gate/up loads h depends on; they arrive while
+    // the rest of h is produced
+    if (tid == 0) arrive_epoch(F, epoch);
+    gather_h<true>(hsrc, g0 * kGroup, g1 * kGroup, tag, S, [&] {
+      if (rowblock) w.load(rowblock, g0, g1, wave, lane);
+    });
+  } else {
+    if (rowblock) w.load(rowblock, g0, g1, wave, lane);
+    if (tid == 0) arrive_epoch(F, epoch);
+    if (kind == 2) pick_weights(F, tag, S);  // the logits are out long before the shared h
+    gather_h(hsrc, g0 * kGroup, g1 * kGroup, tag, S);
+  }
+  const float acc = rowblock ? w.dot_lds(g0, g1, wave, S.xb, S.xb + kFusedXWords / 2, S.hsum) : 0.0f;
+  const float r = reduce_waves4(acc, S.red[0], wave, lane);
+  if (kind == 2) {
+    fused_combine(F, ob, r, tag, S);
+  } else if (wave == 0) {
+    const int n = ob * 64 + lane;
+    if (kind == 0) F.expert_out[(size_t)slot * F.d + n] = r;
+    put_tag(&F.eo_tag[(size_t)slot * F.d + n], __float_as_uint(r), tag);
+  }
 }
 
 // ------------------------------------------------------------------ the kernel
 
 // Work item of a block. Blocks are dealt to the XCDs round robin (block b on XCD
-// b % 8) and the XCDs start the launch one after another, the last several
-// microseconds after the first; the router items head the dependency chain, so
-// they take blocks 0, 8, 16, ... (the first XCD) and the
-// other items the rest in order. Any placement is correct (all blocks are resident at once); this one is
+// b % 8) and XCDs 0 and 1 start first; the router items head the dependency chain,
+// so they take blocks 8j and 8j + 1 (j < n_rt / 2) and the other items the rest in
+// order. Any placement is correct (all blocks are resident at once); this one is
 // faster.
 __device__ __forceinline__ int item_of_block(int b, int n_rt) {
-  if ((int)gridDim.x < 8 * n_rt) return b;  // too few blocks to spread: identity
-  if ((b & 7) == 0 && (b >> 3) < n_rt) return b >> 3;
-  const int before = min(n_rt, (b + 7) >> 3);  // router blocks below b
+  const int R = n_rt / 2;
+  if ((int)gridDim.x < 8 * R || (n_rt & 1)) return b;  // too few blocks to spread: identity
+  const int grp = b >> 3, lane8 = b & 7;
+  if (grp < R && lane8 < 2) return 2 * grp + lane8;
+  const int before = 2 * min(grp, R) + (grp < R ? min(lane8, 2) : 0);  // router blocks below b
   return n_rt + b - before;
 }
 
 template <typename XT>
-__global__ __launch_bounds__(256, 6) void k_decode_fused(FusedArgs F, const XT* __restrict__ x) {
+__global__ __launch_bounds__(256, 4) void k_decode_fused(FusedArgs F, const XT* __restrict__ x) {
   __shared__ FusedSmem S;
+  const uint32_t epoch = read_epoch(F);
+  const uint32_t tag = epoch + 1u;
+  if (blockIdx.x == gridDim.x - 1) return epoch_keeper(F, epoch);
   int b = item_of_block(blockIdx.x, F.n_rt);
-  if (b < F.n_rt) return fused_router(F, x, b, S);
-  b -= F.n_rt;
-  // one call site per item kind, so each body is inlined once
-  if (b < F.n_sg + F.n_rg) {
+  if (b < F.n_rt) {
+    fused_router(F, x, b, tag, epoch, S);
+  } else if ((b -= F.n_rt) < F.n_sg + F.n_rg) {
     const bool routed = b >= F.n_sg;
-    return fused_gateup(F, x, routed ? b - F.n_sg : b, routed, S);
-  }
-  b -= F.n_sg + F.n_rg;
-  if (b < F.n_sd + F.n_rd) {
-    const bool routed = b >= F.n_sd;
-    fused_down(F, routed ? b - F.n_sd : b, routed, S);
+    fused_gateup(F, x, routed ? b - F.n_sg : b, routed, tag, epoch, S);
+  } else if ((b -= F.n_sg + F.n_rg) < F.n_rd) {
+    fused_down<kFusedRoutedGW>(F, b, 0, tag, epoch, S);
+  } else {
+    b -= F.n_rd;
+    fused_down<kFusedSharedGW>(F, b < F.n_sd ? b : b - F.n_sd, b < F.n_sd ? 1 : 2, tag, epoch, S);
   }
 }
 

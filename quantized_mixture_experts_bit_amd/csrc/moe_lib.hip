@@ -64,11 +64,19 @@ DecodeCfg decode_cfg(const moe_shape* s) {
   return c;
 }
 
+// words between the copies of the fused decode's h: one copy rounded up to 4 KiB, plus
+// 4 KiB so the copies start on different channels
+size_t fused_h_stride(const moe_shape* s) {
+  const size_t words = (size_t)(s->top_k + 1) * std::max(s->d_ff, s->d_ff_shared);
+  return (words + 511) / 512 * 512 + 512;
+}
+
 // Workspace layout. The counters come first in a region whose size depends on
 // the shape only (zeroed once, left at zero by every call), so layouts for
 // different row counts never place a counter where another call kept data.
 struct Ws {
-  size_t rt_count, gu_count, dn_count, fused_sync, router_partial, fused_rt, gu_partial, h_hi, h_lo, h_gsum,
+  size_t rt_count, gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, router_partial, gu_partial, h_hi,
+      h_lo, h_gsum,
       shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
@@ -87,8 +95,12 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.gu_count = take(sizeof(uint32_t) * (k + 1) * dc.nbmax);
   w.dn_count = take(sizeof(uint32_t) * (d / 64));
   w.fused_sync = take(sizeof(uint32_t) * kFusedSyncWords);
+  // tagged hand-off words of the fused decode: in the prefix whose layout depends on
+  // the shape only, so no other call ever writes there (a stray tag would read as ready)
+  w.fused_lg = take(sizeof(uint64_t) * kLgCopies * kLgStride);
+  w.fused_h = take(sizeof(uint64_t) * kHCopies * fused_h_stride(s));
+  w.fused_eo = take(sizeof(uint64_t) * (size_t)(k + 1) * d);
   w.router_partial = take(sizeof(double) * rc.nsplit * R * s->n_experts);
-  w.fused_rt = take(sizeof(double) * cdiv(s->d_model / 64, 4) * s->n_experts);
   w.gu_partial = take(sizeof(float) * (size_t)(k + 1) * 2 * dc.nbmax * dc.P * 64);
   w.h_hi = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
   w.h_lo = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
@@ -225,29 +237,42 @@ int fused_capacity() {
 template <typename XT>
 bool launch_decode_fused(const moe_shape* s, const moe_layer* L, const XT* x, const float* off, int32_t* idx,
                          float* w, float* expert_out, float* y, uint16_t* residual, void* ws, hipStream_t st) {
-  // h of one routed slot must fit the workgroup's LDS buffer (12 groups); the
-  // GeGLU rebuild and the combine read at most 4 reduction parts
-  const DecodeCfg dc = decode_cfg(s);
-  if (s->d_ff / 64 > 12 || dc.P > 4 || dc.Ps > 4) return false;
+  // limits of the fused kernel's register and LDS tiling (see decode_fused.h)
+  const int d = s->d_model, f = s->d_ff, fs = s->d_ff_shared;
+  if (d / 64 > kFusedMaxG || f > 64 * 4 * kFusedRoutedGW || fs > 2 * 64 * 4 * kFusedSharedGW) return false;
+  if (sizeof(XT) == 4 && d > kFusedXWords) return false;
   const Ws W = ws_layout(s, 1);
   FusedArgs F;
   memset(&F, 0, sizeof F);
-  F.A = decode_args(s, L, idx, ws, expert_out, w, y, residual);
+  F.pool = L->pool;
+  F.stride = L->blob_stride;
+  F.n_blobs = L->n_blobs;
+  F.slot_table = L->slot_table;
   F.router_blob = L->router_blob;
+  F.shared_blob = L->shared_blob;
   F.offset = off;
-  F.rt_partial = at<double>(ws, W.fused_rt);
+  F.d = d;
+  F.f = f;
+  F.fs = fs;
+  F.E = s->n_experts;
+  F.top_k = s->top_k;
+  F.fmax = std::max(f, fs);
   F.idx_out = idx;
   F.w_out = w;
+  F.expert_out = expert_out;
+  F.y = y;
+  F.residual = residual;
+  F.lg_tag = at<uint64_t>(ws, W.fused_lg);
+  F.h_tag = at<uint64_t>(ws, W.fused_h);
+  F.h_stride = fused_h_stride(s);
+  F.eo_tag = at<uint64_t>(ws, W.fused_eo);
   F.sync = at<uint32_t>(ws, W.fused_sync);
-  F.n_experts = s->n_experts;
-  F.nsplit_r = cdiv(s->d_model / 64, 4);
-  const DecodeArgs& A = F.A;
-  F.n_rt = (s->n_experts / 64) * F.nsplit_r;
-  F.n_sg = 2 * (A.fs / 64) * A.P;
-  F.n_rg = A.top_k * 2 * (A.f / 64) * A.P;
-  F.n_sd = (A.d / 64) * A.Ps;
-  F.n_rd = A.top_k * (A.d / 64);
-  const int grid = F.n_rt + F.n_sg + F.n_rg + F.n_sd + F.n_rd;
+  F.n_rt = s->n_experts / kFusedRouterE;
+  F.n_sg = fs / kFusedRows;
+  F.n_rg = s->top_k * (f / kFusedRows);
+  F.n_rd = s->top_k * (d / 64);
+  F.n_sd = d / 64;
+  const int grid = F.n_rt + F.n_sg + F.n_rg + F.n_rd + 2 * F.n_sd + 1;  // + the epoch keeper
   if (grid > fused_capacity<XT>()) return false;
   k_decode_fused<XT><<<grid, 256, 0, st>>>(F, x);
   return true;

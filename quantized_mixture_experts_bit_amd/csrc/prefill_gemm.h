@@ -40,7 +40,6 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 // native 128-bit vector (HIP's uint4 is a struct: copies of it through register
 // arrays become private-memory copies that stay in scratch)
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // f(integral_constant<int, i>) for i = 0..N-1: ring slots must be compile-time
 // indices, or the register arrays that hold them are demoted to scratch memory

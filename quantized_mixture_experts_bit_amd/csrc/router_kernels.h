@@ -48,19 +48,37 @@ __device__ __forceinline__ uint64_t order_key(double v) {
 // workgroup: rank = the number of experts that beat this one under (key desc,
 // id asc), a strict total order, so the ranks are a permutation. 256 / E threads
 // per expert each count the competitors in their share, reading the keys 16 at a
-// time (one LDS wait per batch). Writes the ids of ranks 0..k-1 to sel_e[rank].
-// key, rank and sel_e are LDS; ends with a barrier.
+// time (one LDS wait per batch). The count runs on the high 32 bits of the keys;
+// a wavefront in which some expert meets another with equal high bits recounts on
+// the whole keys and ids. Writes the ids of ranks 0..k-1 to sel_e[rank]. key,
+// rank and sel_e are LDS; ends with a barrier.
 __device__ __forceinline__ void rank_topk(const uint64_t* key, int E, int k, int (*rank)[256], int* sel_e) {
   const int tid = threadIdx.x;
   const int parts = 256 / E, h = tid / E, per = E / parts, me = tid % E;
   const uint64_t mine = key[me];
-  int r = 0;
+  const uint32_t mh = (uint32_t)(mine >> 32);
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(key);
+  int r = 0, eq = 0;
   for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
-    uint64_t kk[16];
+    uint32_t kh[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kk[i] = key[c0 + i];
+    for (int i = 0; i < 16; ++i) kh[i] = kw[2 * (c0 + i) + 1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r += (kk[i] > mine || (kk[i] == mine && c0 + i < me)) ? 1 : 0;
+    for (int i = 0; i < 16; ++i) {
+      r += kh[i] > mh ? 1 : 0;
+      eq += kh[i] == mh ? 1 : 0;
+    }
+  }
+  if (me / per == h) --eq;  // itself
+  if (__any(eq > 0)) {
+    r = 0;
+    for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
+      uint64_t kk[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) kk[i] = key[c0 + i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r += (kk[i] > mine || (kk[i] == mine && c0 + i < me)) ? 1 : 0;
+    }
   }
   rank[h][me] = r;
   __syncthreads();
