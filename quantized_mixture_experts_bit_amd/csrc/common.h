@@ -58,14 +58,18 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int t) {
 // nib_pair with its two constants held in registers (the mask in an SGPR, the exponent
 // bits in a VGPR): a pair is then one shift and one v_and_or_b32, where literal
 // operands cost a shift, an and and an or.
-struct NibK {
+// kExpo: the exponent bits OR-ed into both halves (0x43004300: bf16 128 + q; 0x64006400:
+// fp16 1024 + q).
+template <uint32_t kExpo = 0x43004300u>
+struct NibKT {
   uint32_t mask, expo;
-  __device__ __forceinline__ NibK() {
+  __device__ __forceinline__ NibKT() {
     asm("s_mov_b32 %0, 0xf000f" : "=s"(mask));
-    asm("v_mov_b32 %0, 0x43004300" : "=v"(expo));
+    asm("v_mov_b32 %0, %1" : "=v"(expo) : "n"(kExpo));
   }
   __device__ __forceinline__ uint32_t pair(uint32_t w, int t) const { return ((w >> (4 * t)) & mask) | expo; }
 };
+using NibK = NibKT<>;
 
 // tanh form of GELU (Hendrycks & Gimpel), fp32
 __device__ __forceinline__ float gelu_tanh(float z) {

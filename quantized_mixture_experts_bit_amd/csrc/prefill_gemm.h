@@ -181,20 +181,19 @@ __device__ __forceinline__ float row_scale(float m) {
 __device__ __forceinline__ uint16_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 // B operand, gate/up: the 8 codes of one packed word as bf16 (128 + q)
-__device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w) {
-  const u32x4_t p = {nib_pair(w, 0), nib_pair(w, 1), nib_pair(w, 2), nib_pair(w, 3)};
+__device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w, const NibK& nk) {
+  const u32x4_t p = {nk.pair(w, 0), nk.pair(w, 1), nk.pair(w, 2), nk.pair(w, 3)};
   return __builtin_bit_cast(bf16x8_t, p);
 }
 
 // B operand, down: the 8 codes of one packed word as exact fp16 values q (0..15):
 // the pair (1024 + q, 1024 + q') is built with a mask and an OR of the exponent of
 // 1024 (0x6400), then 1024 is subtracted with one packed fp16 add per pair.
-__device__ __forceinline__ f16x8_t codes_f16(uint32_t w) {
+__device__ __forceinline__ f16x8_t codes_f16(uint32_t w, const NibKT<0x64006400u>& mk) {
   const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   f16x2_t p[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    p[t] = __builtin_bit_cast(f16x2_t, ((w >> (4 * t)) & 0x000F000Fu) | 0x64006400u) - k1024;
+  for (int t = 0; t < 4; ++t) p[t] = __builtin_bit_cast(f16x2_t, ((w >> (4 * t)) & mk.mask) | mk.expo) - k1024;
   return f16x8_t{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
@@ -343,6 +342,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   // loads near the end are never used). The steady-state loop is
   // straight-line code over kRing groups, so every ring slot keeps its own
   // registers and no wait covers a load younger than the one it needs.
+  const NibK nk;
   auto step = [&](auto jc, int g) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     constexpr int buf = j & 1;
@@ -350,8 +350,8 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
     float s[2], bb[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      bfr[m][0] = codes_bf16(B.cw[j][m][0]);
-      bfr[m][1] = codes_bf16(B.cw[j][m][1]);
+      bfr[m][0] = codes_bf16(B.cw[j][m][0], nk);
+      bfr[m][1] = codes_bf16(B.cw[j][m][1], nk);
       s[m] = bf16_lo(B.sb[j][m]);
       bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
     }
@@ -551,11 +551,12 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   const f16x8_t ones = __builtin_bit_cast(f16x8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
   // one K group, as in the gate/up kernel
+  const NibKT<0x64006400u> nk;
   auto step = [&](auto jc, int g) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     constexpr int buf = j & 1;
-    const f16x8_t b0 = codes_f16(B.cw[j][0][0]);
-    const f16x8_t b1 = codes_f16(B.cw[j][0][1]);
+    const f16x8_t b0 = codes_f16(B.cw[j][0][0], nk);
+    const f16x8_t b1 = codes_f16(B.cw[j][0][1], nk);
     const float s = bf16_lo(B.sb[j][0]);
     const float bp = bf16_hi(B.sb[j][0]);
     B.load(jc, wbase, min(g + kRing, G - 1), wrow, lane);
