@@ -39,18 +39,6 @@ bool shape_ok(const moe_shape* s) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// router split: rows per workgroup and reduction splits (16 groups each)
-struct RouterCfg {
-  int rpw, nsplit;
-};
-RouterCfg router_cfg(const moe_shape* s, int rows) {
-  RouterCfg c;
-  c.rpw = rows <= 4 ? 1 : 2;
-  c.nsplit = cdiv(s->d_model / 64, kRouterGPB);
-  return c;
-}
-// most activation rows a call can take: rows * top_k < 65536
-inline int max_rows(const moe_shape* s) { return 65535 / s->top_k; }
 
 struct DecodeCfg {
   int P, Ps, fmax, nbmax;
@@ -75,13 +63,12 @@ size_t fused_h_stride(const moe_shape* s) {
 // the shape only (zeroed once, left at zero by every call), so layouts for
 // different row counts never place a counter where another call kept data.
 struct Ws {
-  size_t rt_count, gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, router_partial, gu_partial, h_hi,
+  size_t gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, router_partial, gu_partial, h_hi,
       h_lo, h_gsum,
       shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
-  const RouterCfg rc = router_cfg(s, std::max(rows, 1));
   const int k = s->top_k, d = s->d_model;
   const size_t R = (size_t)std::max(rows, 1);
   Ws w;
@@ -91,7 +78,6 @@ Ws ws_layout(const moe_shape* s, int rows) {
     o = align256(o + bytes);
     return at;
   };
-  w.rt_count = take(sizeof(uint32_t) * max_rows(s));
   w.gu_count = take(sizeof(uint32_t) * (k + 1) * dc.nbmax);
   w.dn_count = take(sizeof(uint32_t) * (d / 64));
   w.fused_sync = take(sizeof(uint32_t) * kFusedSyncWords);
@@ -100,7 +86,7 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.fused_lg = take(sizeof(uint64_t) * kLgCopies * kLgStride);
   w.fused_h = take(sizeof(uint64_t) * kHCopies * fused_h_stride(s));
   w.fused_eo = take(sizeof(uint64_t) * (size_t)(k + 1) * d);
-  w.router_partial = take(sizeof(double) * rc.nsplit * R * s->n_experts);
+  w.router_partial = take(sizeof(double) * kRouterSplits * R * s->n_experts);
   w.gu_partial = take(sizeof(float) * (size_t)(k + 1) * 2 * dc.nbmax * dc.P * 64);
   w.h_hi = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
   w.h_lo = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
@@ -153,17 +139,11 @@ moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ER
 template <typename XT>
 void launch_router(const moe_shape* s, const moe_layer* L, const XT* x, int rows, const float* off, int32_t* idx,
                    float* w, double* logits, void* ws, hipStream_t st) {
-  const RouterCfg rc = router_cfg(s, rows);
   const Ws W = ws_layout(s, rows);
   double* part = at<double>(ws, W.router_partial);
-  uint32_t* cnt = at<uint32_t>(ws, W.rt_count);
-  dim3 grid(s->n_experts / 64, rc.nsplit, cdiv(rows, rc.rpw));
-  if (rc.rpw == 1)
-    k_router<XT, 1><<<grid, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, s->top_k, rc.nsplit,
-                                          off, part, cnt, idx, w, logits);
-  else
-    k_router<XT, 2><<<grid, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, s->top_k, rc.nsplit,
-                                          off, part, cnt, idx, w, logits);
+  const int blocks = cdiv(rows, 16) * (s->n_experts / 16) * kRouterSplits;
+  k_router_logits<XT><<<blocks, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, part);
+  k_router_select<<<rows, 256, 0, st>>>(part, rows, s->n_experts, s->top_k, off, idx, w, logits);
 }
 
 DecodeArgs decode_args(const moe_shape* s, const moe_layer* L, const int32_t* idx, void* ws, float* expert_out,

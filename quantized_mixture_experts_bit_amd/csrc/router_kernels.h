@@ -16,16 +16,11 @@ namespace qmoe {
 __device__ __forceinline__ float x_as_f32(float v) { return v; }
 __device__ __forceinline__ float x_as_f32(uint16_t v) { return bf16_to_f32(v); }
 
-constexpr int kRouterGPW = 4;                   // groups per wavefront
-constexpr int kRouterGPB = 4 * kRouterGPW;      // groups per workgroup (4 waves)
-constexpr int kMaxRouterSplits = 6;             // d_model <= 6144: at most 96 groups / 16
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void st_agent_d(double* p, double v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double ld_agent_d(const double* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+constexpr int kRouterSplits = 4;                  // workgroups along the reduction
+constexpr int kRouterParts = 4 * kRouterSplits;   // wavefronts along the reduction
+constexpr int kRouterMaxGPP = 6;                  // groups per part: d_model <= 6144
 
 // a beats b: larger logit, ties to the lower expert id. A NaN logit ranks below
 // every number (as -inf), so this is a strict total order on (logit, id) and the
@@ -90,124 +85,139 @@ __device__ __forceinline__ void rank_topk(const uint64_t* key, int E, int k, int
   __syncthreads();
 }
 
-// grid (n_experts/64, nsplit, ceil(rows/RPW)), block 256. Workgroup (nb, split, chunk):
-// lane = expert nb*64 + lane, wave w = groups [split*16 + 4w, +4) of the reduction,
-// rows [chunk*RPW, +RPW). Partial logits go to `partial` [nsplit][rows][E]; the
-// last workgroup of a row chunk (arrival counter) sums them in split order, adds
-// the offset and picks the top-k of each row of the chunk (rank_topk).
-template <typename XT, int RPW>
-__global__ __launch_bounds__(256) void k_router(const uint8_t* __restrict__ router, const XT* __restrict__ x,
-                                                int rows, int d, int n_experts, int top_k, int nsplit,
-                                                const float* __restrict__ offset, double* __restrict__ partial,
-                                                uint32_t* __restrict__ counters, int32_t* __restrict__ topk_idx,
-                                                float* __restrict__ topk_w, double* __restrict__ logits_out) {
-  __shared__ double xs[RPW][kRouterGPB * kGroup];
-  __shared__ double red[4][RPW][64];
-  __shared__ int last;
+__device__ __forceinline__ uint32_t u4_at(const uint4& u, int c) {
+  return c == 0 ? u.x : c == 1 ? u.y : c == 2 ? u.z : u.w;
+}
+
+// 16 consecutive activations of one row, loaded raw (32 bytes of bf16, 64 of fp32).
+template <typename XT>
+struct XRow16;
+template <>
+struct XRow16<uint16_t> {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v[0] = ldg16(reinterpret_cast<const uint8_t*>(p));
+    v[1] = ldg16(reinterpret_cast<const uint8_t*>(p) + 16);
+  }
+  __device__ __forceinline__ double at(int t) const {
+    const uint32_t w = u4_at(v[t >> 3], (t >> 1) & 3);
+    return (double)((t & 1) ? bf16_hi(w) : bf16_lo(w));
+  }
+};
+template <>
+struct XRow16<float> {
+  uint4 v[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = ldg16(reinterpret_cast<const uint8_t*>(p) + 16 * c);
+  }
+  __device__ __forceinline__ double at(int t) const { return (double)__uint_as_float(u4_at(v[t >> 2], t & 3)); }
+};
+
+// Router logits over part of the reduction, on the fp64 matrix cores. Grid
+// ceil(rows/16) * (n_experts/16) * kRouterSplits workgroups of 256 threads; workgroup
+// (rt, et, split) computes the block rows [16 rt, +16) x experts [16 et, +16) over the
+// groups g with g % kRouterParts in [4 split, +4), wavefront w taking g % kRouterParts ==
+// 4 split + w. Each group is 16 steps of the 16x16x4 fp64 MFMA: lane l supplies the
+// activation of row l%16 and the dequantised weight (s*q + b, exact in fp64) of expert
+// l%16 at the same column, 16 (l/16) + t in step t, i.e. one quarter of the expert's
+// packed 8-bit tile row and the matching 32 (bf16) or 64 (fp32) bytes of the activation
+// row. All products are exact in fp64. The four wavefront sums are added in wave order
+// and stored to partial[split][row][e]; rows past the end read the last row and are not
+// stored.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_router_logits(const uint8_t* __restrict__ router, const XT* __restrict__ x,
+                                                       int rows, int d, int n_experts,
+                                                       double* __restrict__ partial) {
+  __shared__ double red[4][256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = blockIdx.x, split = blockIdx.y, chunk = blockIdx.z;
-  const int G = d / kGroup;
-  const int gs0 = split * kRouterGPB;
-  const int ngs = min(G - gs0, kRouterGPB);
-  const int r0 = chunk * RPW;
-  const int nr = min(rows - r0, RPW);
+  const int n_et = n_experts >> 4;
+  int b = blockIdx.x;
+  const int split = b % kRouterSplits;
+  b /= kRouterSplits;
+  const int et = b % n_et, rt = b / n_et;
+  const int G = d / kGroup, part = split * 4 + wave;
+  const int i = lane & 15, j = lane >> 4;
+  const int e = et * 16 + i;
+  const int row = min(rt * 16 + i, rows - 1);
+  const uint8_t* wt = router + (size_t)(e >> 6) * G * kTile8 + j * 1024 + (e & 63) * 16;
+  const uint8_t* st = router + (size_t)(e >> 6) * G * kTile8 + kTile8Codes + (e & 63) * 4;
+  const XT* xr = x + (size_t)row * d + 16 * j;
 
-  // this wave's codes and scales, all loads issued before any arithmetic
-  const int gw0 = gs0 + wave * kRouterGPW;
-  const int ngw = max(0, min(kRouterGPW, gs0 + ngs - gw0));
-  uint4 q[kRouterGPW][4];
-  uint32_t sbw[kRouterGPW];
+  // every load of the part issued before any arithmetic
+  uint4 q[kRouterMaxGPP];
+  uint32_t sb[kRouterMaxGPP];
+  XRow16<XT> xv[kRouterMaxGPP];
 #pragma unroll
-  for (int i = 0; i < kRouterGPW; ++i) {
-    if (i < ngw) {
-      const uint8_t* tile = router + ((size_t)nb * G + gw0 + i) * kTile8;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) q[i][c] = ldg16(tile + c * 1024 + lane * 16);
-      sbw[i] = ldg4(tile + kTile8Codes + lane * 4);
+  for (int n = 0; n < kRouterMaxGPP; ++n) {
+    const int g = part + n * kRouterParts;
+    if (g < G) {
+      q[n] = ldg16(wt + (size_t)g * kTile8);
+      sb[n] = ldg4(st + (size_t)g * kTile8);
+      xv[n].load(xr + g * kGroup);
     }
   }
-  for (int i = tid; i < RPW * kRouterGPB * kGroup; i += 256) {
-    const int r = i / (kRouterGPB * kGroup), c = i % (kRouterGPB * kGroup);
-    xs[r][c] = (r < nr && c < ngs * kGroup) ? (double)x_as_f32(x[(size_t)(r0 + r) * d + gs0 * kGroup + c]) : 0.0;
-  }
-  __syncthreads();
-
-  double acc[RPW];
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0;
+  for (int n = 0; n < kRouterMaxGPP; ++n) {
+    if (part + n * kRouterParts < G) {
+      const double s = (double)bf16_lo(sb[n]), bb = (double)bf16_hi(sb[n]);
 #pragma unroll
-  for (int i = 0; i < kRouterGPW; ++i) {
-    if (i < ngw) {
-      const double s = (double)bf16_lo(sbw[i]), b = (double)bf16_hi(sbw[i]);
-      const int cbase = (wave * kRouterGPW + i) * kGroup;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t words[4] = {q[i][c].x, q[i][c].y, q[i][c].z, q[i][c].w};
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const double wv = fma(s, (double)((words[j >> 2] >> (8 * (j & 3))) & 0xffu), b);
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) acc[r] = fma(wv, xs[r][cbase + c * 16 + j], acc[r]);
-        }
+      for (int t = 0; t < 16; ++t) {
+        const uint32_t code = (u4_at(q[n], t >> 2) >> (8 * (t & 3))) & 0xffu;
+        const double wv = fma(s, (double)code, bb);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[n].at(t), wv, acc, 0, 0, 0);
       }
     }
   }
+  // result layout of the 16x16 fp64 MFMA: element r of lane l is row l/16 + 4 r, column l%16
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) red[wave][r][lane] = acc[r];
+  for (int r = 0; r < 4; ++r) red[wave][(j + 4 * r) * 16 + i] = acc[r];
   __syncthreads();
-  if (wave == 0) {
-    const int e = nb * 64 + lane;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      if (r < nr)
-        st_agent_d(&partial[((size_t)split * rows + r0 + r) * n_experts + e],
-                   ((red[0][r][lane] + red[1][r][lane]) + red[2][r][lane]) + red[3][r][lane]);
-    wait_mem();
-    if (lane == 0)
-      last = (arrive(&counters[chunk]) == (uint32_t)((n_experts / 64) * nsplit - 1));
-  }
-  __syncthreads();
-  if (!last) return;
+  const int orow = rt * 16 + (tid >> 4);
+  if (orow < rows)
+    partial[((size_t)split * rows + orow) * n_experts + et * 16 + (tid & 15)] =
+        ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
 
-  // ---- logits of the chunk's rows (partials summed in split order, + offset), then
-  // per row: ranking by all 256 threads and the softmax over the picks
-  __shared__ double lgv[RPW][256];
+// One workgroup (256 threads) per row: the row's logits are the kRouterSplits partial
+// sums added in split order, plus the offset; then the top-k by rank (rank_topk) and
+// the softmax over the picks (fp64, in pick order).
+__global__ __launch_bounds__(256) void k_router_select(const double* __restrict__ partial, int rows, int n_experts,
+                                                       int top_k, const float* __restrict__ offset,
+                                                       int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                       double* __restrict__ logits_out) {
+  __shared__ double lgv[256];
   __shared__ uint64_t key[256];
   __shared__ int rank[4][256];
   __shared__ int sel_e[16];
-  for (int i = tid; i < nr * n_experts; i += 256) {
-    const int r = i / n_experts, e = i % n_experts, row = r0 + r;
-    double pv[kMaxRouterSplits];  // all loads in flight at once, summed in split order
+  const int tid = threadIdx.x, row = blockIdx.x;
+  if (tid < n_experts) {
+    double pv[kRouterSplits];
 #pragma unroll
-    for (int sp = 0; sp < kMaxRouterSplits; ++sp)
-      pv[sp] = sp < nsplit ? ld_agent_d(&partial[((size_t)sp * rows + row) * n_experts + e]) : 0.0;
-    double a = 0.0;
+    for (int sp = 0; sp < kRouterSplits; ++sp) pv[sp] = partial[((size_t)sp * rows + row) * n_experts + tid];
+    double a = pv[0];
 #pragma unroll
-    for (int sp = 0; sp < kMaxRouterSplits; ++sp) a += pv[sp];
-    if (offset) a += (double)offset[e];
-    lgv[r][e] = a;
-    if (logits_out) logits_out[(size_t)row * n_experts + e] = a;
+    for (int sp = 1; sp < kRouterSplits; ++sp) a += pv[sp];
+    if (offset) a += (double)offset[tid];
+    lgv[tid] = a;
+    key[tid] = order_key(a);
+    if (logits_out) logits_out[(size_t)row * n_experts + tid] = a;
   }
-  for (int r = 0; r < nr; ++r) {
-    __syncthreads();  // lgv complete; the previous row's picks are read
-    if (tid < n_experts) key[tid] = order_key(lgv[r][tid]);
-    __syncthreads();
-    rank_topk(key, n_experts, top_k, rank, sel_e);
-    if (wave == 0) {
-      // softmax over the picks in pick order (fp64), fixed summation order
-      const int row = r0 + r;
-      const int se = lane < top_k ? sel_e[lane] : 0;
-      const double ex = lane < top_k ? exp(lgv[r][se] - lgv[r][sel_e[0]]) : 0.0;
-      double sum = 0.0;
-      for (int t = 0; t < top_k; ++t) sum += __shfl(ex, t, 64);
-      if (lane < top_k) {
-        topk_idx[(size_t)row * top_k + lane] = se;
-        topk_w[(size_t)row * top_k + lane] = (float)(ex / sum);
-      }
+  __syncthreads();
+  rank_topk(key, n_experts, top_k, rank, sel_e);
+  if (tid < 64) {
+    const int lane = tid;
+    const int se = lane < top_k ? sel_e[lane] : 0;
+    const double ex = lane < top_k ? exp(lgv[se] - lgv[sel_e[0]]) : 0.0;
+    double sum = 0.0;
+    for (int t = 0; t < top_k; ++t) sum += __shfl(ex, t, 64);
+    if (lane < top_k) {
+      topk_idx[(size_t)row * top_k + lane] = se;
+      topk_w[(size_t)row * top_k + lane] = (float)(ex / sum);
     }
   }
-  if (tid == 0) counters[chunk] = 0u;
 }
 
 }  // namespace qmoe
