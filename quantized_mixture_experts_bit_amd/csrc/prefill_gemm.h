@@ -111,7 +111,7 @@ __device__ __forceinline__ int tile_map_init(const PrefillArgs& A, TileMap& M) {
   }
   M.excl = incl - mine;
   M.incl = incl;
-  return __shfl(incl, 63, 64);
+  return __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
 }
 
 // 64-row tile -> (expert, first sorted position, row count, weights); every lane
@@ -138,11 +138,12 @@ __device__ __forceinline__ bool tile_at(const PrefillArgs& A, const TileMap& M, 
       t += nt;
     }
   }
-  T.e = __shfl(e, owner, 64);
-  T.m0 = __shfl(m0, owner, 64);
-  T.mrows = __shfl(mr, owner, 64);
+  // uniform values: kept in scalar registers, so the weight addresses are scalar bases
+  T.e = __builtin_amdgcn_readfirstlane(__shfl(e, owner, 64));
+  T.m0 = __builtin_amdgcn_readfirstlane(__shfl(m0, owner, 64));
+  T.mrows = __builtin_amdgcn_readfirstlane(__shfl(mr, owner, 64));
   T.F = A.f;
-  T.blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, T.e, A.n_experts);
+  T.blob = uniform_ptr(expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, T.e, A.n_experts));
   return T.blob != nullptr;
 }
 
@@ -211,19 +212,25 @@ __device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
 
 // Weight fragments of NM matrices in a ring of kRing groups: for wave row `row`
 // (0..63 within the 64-row block), the two code words of k-halves 0 and 1 and the
-// (scale, bias) pair, from tile g at wbase[m] + g * kTile4.
+// (scale, bias) pair, from tile g of the column block whose tiles start at the base
+// of wres[m]. The lane offsets are fixed; the group enters as a scalar offset.
 template <int NM>
 struct BRing {
   uint32_t cw[kRing][NM][2];
   uint32_t sb[kRing][NM];
+  uint32_t vc, vs;  // lane offsets of the code word and of (s, b) within a tile
+  __device__ __forceinline__ void init(int row, int lane) {
+    vc = row * 16 + (lane >> 4) * 4;
+    vs = kTile4Codes + row * 4;
+  }
   template <int slot>
-  __device__ __forceinline__ void load(ic<slot>, const uint8_t* const* wbase, int g, int row, int lane) {
+  __device__ __forceinline__ void load(ic<slot>, const rsrc_t* wres, int g) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const uint8_t* t = wbase[m] + (uint64_t)g * kTile4;
-      cw[slot][m][0] = ldg4(t + row * 16 + (lane >> 4) * 4);
-      cw[slot][m][1] = ldg4(t + 1024 + row * 16 + (lane >> 4) * 4);
-      sb[slot][m] = ldg4(t + kTile4Codes + row * 4);
+      const uint32_t so = (uint32_t)g * kTile4;
+      cw[slot][m][0] = bld4(wres[m], vc, so);
+      cw[slot][m][1] = bld4(wres[m], vc + 1024, so);
+      sb[slot][m] = bld4(wres[m], vs, so);
     }
   }
 };
@@ -260,11 +267,13 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
 
   // weight rows of this wave: row 16*wave + lane%16 of the 64-row block fc of gate and up
   const int wrow = 16 * wave + (lane & 15);
-  const uint8_t* wbase[2];
+  rsrc_t wres[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
-    wbase[m] = T.blob + (uint64_t)m * m4_bytes(T.F, A.d) + (uint64_t)fc * G * kTile4;
+    wres[m] = buf_rsrc(uniform_ptr(T.blob) + (uint64_t)m * m4_bytes(T.F, A.d) + (uint64_t)fc * G * kTile4,
+                       (uint32_t)G * kTile4);
   BRing<2> B;
+  B.init(wrow, lane);
 
   // activation staging: thread -> tile row tid/4, 16 values at column (tid%4)*16.
   // Rows past the tile's end repeat its first row: MFMA output rows depend on their
@@ -272,13 +281,13 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   const int xr = tid >> 2, xq = tid & 3;
   const int xt = xr < T.mrows ? xr : 0;
   const int xsrc = T.e >= 0 ? A.perm[T.m0 + xt] / A.top_k : T.m0 + xt;
-  const XT* xrow = x + (size_t)xsrc * A.d + xq * 16;
+  const rsrc_t xres = buf_rsrc(x, (uint32_t)((size_t)A.rows * A.d * sizeof(XT)));
+  const uint32_t xvo = (uint32_t)(((size_t)xsrc * A.d + xq * 16) * sizeof(XT));
   u32x4_t xa[RA][NV];
   auto aload = [&](auto sc, int g) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-      xa[slot][v] = *reinterpret_cast<const u32x4_t*>(xrow + g * kGroup + v * (16 / sizeof(XT)));
+    for (int v = 0; v < NV; ++v) xa[slot][v] = bld16(xres, xvo + 16 * v, (uint32_t)(g * kGroup * sizeof(XT)));
   };
   auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
@@ -319,7 +328,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   aload(ic<0>{}, 0);
   static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
-    B.load(jc, wbase, min(j, G - 1), wrow, lane);
+    B.load(jc, wres, min(j, G - 1));
     if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(j + 1, G - 1));
     if constexpr (j + 1 == RA) {
       astore(ic<0>{}, 0);
@@ -355,7 +364,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
       s[m] = bf16_lo(B.sb[j][m]);
       bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
     }
-    B.load(jc, wbase, min(g + kRing, G - 1), wrow, lane);
+    B.load(jc, wres, min(g + kRing, G - 1));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if (mb < nmb) {
@@ -511,19 +520,23 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   const float* hsc = shared ? A.hsc + P : A.hsc;
 
   const int wrow = 16 * wave + (lane & 15);
-  const uint8_t* wbase[1] = {T.blob + 2 * m4_bytes(F, A.d) + (uint64_t)nb * G * kTile4};
+  const rsrc_t wres[1] = {
+      buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nb * G * kTile4, (uint32_t)G * kTile4)};
   BRing<1> B;
+  B.init(wrow, lane);
   if (tid < 64) rowinv[tid] = tid < T.mrows ? 1.0f / hsc[T.m0 + tid] : 1.0f;  // exact: powers of two
 
   // H staging: thread -> tile row tid/4, 16 halfs at column (tid%4)*16; rows past
   // the tile's end repeat its first row (see the gate/up kernel)
   const int hr = tid >> 2, hq = tid & 3;
-  const uint16_t* hrow = Hh + (size_t)(T.m0 + (hr < T.mrows ? hr : 0)) * F + hq * 16;
+  const rsrc_t hres = buf_rsrc(Hh, (uint32_t)((size_t)(shared ? A.rows : P) * F * sizeof(uint16_t)));
+  const uint32_t hvo = (uint32_t)(((size_t)(T.m0 + (hr < T.mrows ? hr : 0)) * F + hq * 16) * sizeof(uint16_t));
   u32x4_t ha[RA][2];
   auto aload = [&](auto sc, int g) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
-    ha[slot][0] = *reinterpret_cast<const u32x4_t*>(hrow + g * kGroup);
-    ha[slot][1] = *reinterpret_cast<const u32x4_t*>(hrow + g * kGroup + 8);
+    const uint32_t so = (uint32_t)(g * kGroup * sizeof(uint16_t));
+    ha[slot][0] = bld16(hres, hvo, so);
+    ha[slot][1] = bld16(hres, hvo + 16, so);
   };
   auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
@@ -536,7 +549,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   aload(ic<0>{}, 0);
   static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
-    B.load(jc, wbase, min(j, G - 1), wrow, lane);
+    B.load(jc, wres, min(j, G - 1));
     if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(j + 1, G - 1));
     if constexpr (j + 1 == RA) {
       astore(ic<0>{}, 0);
@@ -559,7 +572,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     const f16x8_t b1 = codes_f16(B.cw[j][0][1], nk);
     const float s = bf16_lo(B.sb[j][0]);
     const float bp = bf16_hi(B.sb[j][0]);
-    B.load(jc, wbase, min(g + kRing, G - 1), wrow, lane);
+    B.load(jc, wres, min(g + kRing, G - 1));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if (mb < nmb) {
