@@ -337,97 +337,110 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   });
   __syncthreads();
 
-  f32x4_t acc[4][2];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    zero_acc(acc[mb][0]);
-    zero_acc(acc[mb][1]);
-  }
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-
-  // One K group: MFMAs from LDS buffer j&1 and weight slot j; then the weight
-  // slot is refilled with group g + kRing and the activation slot staged next is
-  // refilled with group g + 1 + RA, both clamped to the last group (the surplus
-  // loads near the end are never used). The steady-state loop is
-  // straight-line code over kRing groups, so every ring slot keeps its own
-  // registers and no wait covers a load younger than the one it needs.
-  const NibK nk;
-  auto step = [&](auto jc, int g) __attribute__((always_inline)) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int buf = j & 1;
-    bf16x8_t bfr[2][2];
-    float s[2], bb[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bfr[m][0] = codes_bf16(B.cw[j][m][0], nk);
-      bfr[m][1] = codes_bf16(B.cw[j][m][1], nk);
-      s[m] = bf16_lo(B.sb[j][m]);
-      bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
+  // The compute is compiled for NMB = 1, 2 and 4 blocks of 16 rows (3 runs as 4), so
+  // the blocks' MFMAs and epilogue FMAs form straight-line code the scheduler can
+  // interleave, instead of one branch per block.
+  auto run = [&](auto nc) __attribute__((always_inline)) {
+    constexpr int NMB = decltype(nc)::value;
+    f32x4_t acc[NMB][2];
+  #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      zero_acc(acc[mb][0]);
+      zero_acc(acc[mb][1]);
     }
-    B.load(jc, wres, min(g + kRing, G - 1));
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb < nmb) {
-        const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
-        const bf16x8_t a0 = lds_frag<bf16x8_t>(&Xs[buf][ao]);
-        const bf16x8_t a1 = lds_frag<bf16x8_t>(&Xs[buf][ao + 32]);
-        f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
-        f32x4_t t[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) t[m] = mfma(a1, bfr[m][1], mfma(a0, bfr[m][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
-        if (LO) {
-          const bf16x8_t l0 = lds_frag<bf16x8_t>(&Xls[buf][ao]);
-          const bf16x8_t l1 = lds_frag<bf16x8_t>(&Xls[buf][ao + 32]);
-          ag = mfma(l1, ones, mfma(l0, ones, ag));
-#pragma unroll
-          for (int m = 0; m < 2; ++m) t[m] = mfma(l1, bfr[m][1], mfma(l0, bfr[m][0], t[m]));
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+    // One K group: MFMAs from LDS buffer j&1 and weight slot j; then the weight
+    // slot is refilled with group g + kRing and the activation slot staged next is
+    // refilled with group g + 1 + RA, both clamped to the last group (the surplus
+    // loads near the end are never used). The steady-state loop is
+    // straight-line code over kRing groups, so every ring slot keeps its own
+    // registers and no wait covers a load younger than the one it needs.
+    const NibK nk;
+    auto step = [&](auto jc, int g) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int buf = j & 1;
+      bf16x8_t bfr[2][2];
+      float s[2], bb[2];
+  #pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bfr[m][0] = codes_bf16(B.cw[j][m][0], nk);
+        bfr[m][1] = codes_bf16(B.cw[j][m][1], nk);
+        s[m] = bf16_lo(B.sb[j][m]);
+        bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
+      }
+      B.load(jc, wres, min(g + kRing, G - 1));
+  #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        {
+          const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
+          const bf16x8_t a0 = lds_frag<bf16x8_t>(&Xs[buf][ao]);
+          const bf16x8_t a1 = lds_frag<bf16x8_t>(&Xs[buf][ao + 32]);
+          f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          f32x4_t t[2];
+  #pragma unroll
+          for (int m = 0; m < 2; ++m) t[m] = mfma(a1, bfr[m][1], mfma(a0, bfr[m][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          if (LO) {
+            const bf16x8_t l0 = lds_frag<bf16x8_t>(&Xls[buf][ao]);
+            const bf16x8_t l1 = lds_frag<bf16x8_t>(&Xls[buf][ao + 32]);
+            ag = mfma(l1, ones, mfma(l0, ones, ag));
+  #pragma unroll
+            for (int m = 0; m < 2; ++m) t[m] = mfma(l1, bfr[m][1], mfma(l0, bfr[m][0], t[m]));
+          }
+  #pragma unroll
+          for (int m = 0; m < 2; ++m)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[m][i], fmaf(bb[m], ag[i], acc[mb][m][i]));
         }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[m][i], fmaf(bb[m], ag[i], acc[mb][m][i]));
       }
+      // next activation group into the other buffer (its readers passed the last barrier)
+      astore(ic<(j + 1) % RA>{}, buf ^ 1);
+      aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, G - 1));
+      __syncthreads();
+    };
+    int g0 = 0;
+    for (; g0 + kRing <= G; g0 += kRing) {
+      step(ic<0>{}, g0);
+      step(ic<1>{}, g0 + 1);
+      step(ic<2>{}, g0 + 2);
+      step(ic<3>{}, g0 + 3);
     }
-    // next activation group into the other buffer (its readers passed the last barrier)
-    astore(ic<(j + 1) % RA>{}, buf ^ 1);
-    aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, G - 1));
-    __syncthreads();
-  };
-  int g0 = 0;
-  for (; g0 + kRing <= G; g0 += kRing) {
-    step(ic<0>{}, g0);
-    step(ic<1>{}, g0 + 1);
-    step(ic<2>{}, g0 + 2);
-    step(ic<3>{}, g0 + 3);
-  }
-  // the last G % kRing groups
-  if (g0 < G) step(ic<0>{}, g0);
-  if (g0 + 1 < G) step(ic<1>{}, g0 + 1);
-  if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
+    // the last G % kRing groups
+    if (g0 < G) step(ic<0>{}, g0);
+    if (g0 + 1 < G) step(ic<1>{}, g0 + 1);
+    if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
 
-  // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16
-  float* H = shared ? A.Hs : A.H;
-  float* hmaxp = shared ? A.hmaxp + (size_t)A.rows * A.top_k * (A.f / 64) : A.hmaxp;
-  const int F = T.F, nG = F / 64;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mb + 4 * (lane >> 4) + i;
-      float h = 0.0f;
-      if (r < T.mrows) {
-        h = gelu_tanh(acc[mb][0][i]) * acc[mb][1][i];
-        H[(size_t)(T.m0 + r) * F + fc * 64 + 16 * wave + (lane & 15)] = h;
+    // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16
+    float* H = shared ? A.Hs : A.H;
+    float* hmaxp = shared ? A.hmaxp + (size_t)A.rows * A.top_k * (A.f / 64) : A.hmaxp;
+    const int F = T.F, nG = F / 64;
+  #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mb + 4 * (lane >> 4) + i;
+        float h = 0.0f;
+        if (r < T.mrows) {
+          h = gelu_tanh(acc[mb][0][i]) * acc[mb][1][i];
+          H[(size_t)(T.m0 + r) * F + fc * 64 + 16 * wave + (lane & 15)] = h;
+        }
+        // max |h| over the 16 lanes holding this row
+        float mx = fabsf(h);
+  #pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        if ((lane & 15) == 0) hmL[wave][r] = mx;
       }
-      // max |h| over the 16 lanes holding this row
-      float mx = fabsf(h);
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-      if ((lane & 15) == 0) hmL[wave][r] = mx;
-    }
-  __syncthreads();
-  if (tid < T.mrows)
-    hmaxp[(size_t)(T.m0 + tid) * nG + fc] = fmaxf(fmaxf(hmL[0][tid], hmL[1][tid]), fmaxf(hmL[2][tid], hmL[3][tid]));
+    __syncthreads();
+    if (tid < T.mrows)
+      hmaxp[(size_t)(T.m0 + tid) * nG + fc] = fmaxf(fmaxf(hmL[0][tid], hmL[1][tid]), fmaxf(hmL[2][tid], hmL[3][tid]));
+
+  };
+  if (nmb == 1)
+    run(ic<1>{});
+  else if (nmb == 2)
+    run(ic<2>{});
+  else
+    run(ic<4>{});
 }
 
 // Persistent: a grid sized to what the chip holds at once walks the work items

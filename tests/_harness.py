@@ -25,6 +25,12 @@ def device():
     return torch.device("cuda:0")
 
 
+# shapes at the edges of what the library accepts: the most experts and picks (256, 16)
+# and few experts, few picks, groups that do not fill a 4-group block
+WIDE = synth.MoeShape(1024, 256, 768, n_experts=256, top_k=16)
+NARROW = synth.MoeShape(768, 192, 320, n_experts=64, top_k=4)
+
+
 def get_layer(shape, seed=0, layer=0, variant=synth.Variant()):
     """(canonical layer, oracle layer, device layer), cached per process."""
     key = (shape, seed, layer, variant)

@@ -7,8 +7,8 @@ import torch
 
 import oracle as O
 import synth
-from _harness import (REL_TOL, check_topk, empty_f32, empty_i32, get_layer, rel_err, to_dev_x, workspace,
-                      device)
+from _harness import (NARROW, REL_TOL, WIDE, check_topk, empty_f32, empty_i32, get_layer, rel_err, to_dev_x,
+                      workspace, device)
 
 pytestmark = pytest.mark.gpu
 q = pytest.importorskip("quantized_mixture_experts_bit_amd")
@@ -20,6 +20,8 @@ CASES = [
     pytest.param(synth.TINY, "bf16", SOFT, id="tiny-bf16-soft"),
     pytest.param(synth.GEMMA4, "bf16", synth.Variant(), id="gemma4-bf16"),
     pytest.param(synth.GEMMA4, "bf16", SOFT, id="gemma4-bf16-soft"),
+    pytest.param(WIDE, "bf16", SOFT, id="wide256x16-bf16-soft"),
+    pytest.param(NARROW, "f32", SOFT, id="narrow64x4-f32-soft"),
 ]
 
 

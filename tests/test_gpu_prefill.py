@@ -6,8 +6,8 @@ import torch
 
 import oracle as O
 import synth
-from _harness import (REL_TOL, check_topk, device, empty_f32, empty_i32, get_layer, rel_err, to_dev_x,
-                      workspace)
+from _harness import (NARROW, REL_TOL, WIDE, check_topk, device, empty_f32, empty_i32, get_layer, rel_err,
+                      to_dev_x, workspace)
 
 pytestmark = pytest.mark.gpu
 q = pytest.importorskip("quantized_mixture_experts_bit_amd")
@@ -55,6 +55,11 @@ PREFILL_CASES = [
     pytest.param(synth.GEMMA4, 128, "bf16", None, "zipf", id="gemma4-128rows-bf16-zipf"),
     pytest.param(synth.GEMMA4, 256, "bf16", None, "zipf", id="gemma4-256rows-bf16-zipf"),
     pytest.param(synth.GEMMA4, 19, "bf16", synth.Variant(router_scale_log2=-6), None, id="gemma4-19rows-soft"),
+    pytest.param(synth.GEMMA4, 64, "f32", None, "zipf", id="gemma4-64rows-f32-zipf"),
+    pytest.param(WIDE, 40, "bf16", synth.Variant(router_scale_log2=-6), None, id="wide256x16-40rows-soft"),
+    pytest.param(NARROW, 33, "f32", synth.Variant(router_scale_log2=-6), None, id="narrow64x4-33rows-f32-soft"),
+    # the most rows a call takes (rows * top_k < 65536): every expert gets many 64-row tiles
+    pytest.param(synth.GEMMA4, 65535 // 8, "bf16", None, None, id="gemma4-8191rows-max"),
 ]
 
 
