@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=128)
     ap.add_argument("--stack-rows", type=int, default=256, help="rows per chunk of the 30-layer prefill stack")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--sweep-chunks", default="", metavar="R1,R2,...",
+                    help="also time prefill chunks of these row counts (reported under prefill_chunk_sweep)")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="rows in the oracle's timed CPU sample")
@@ -217,13 +219,15 @@ def main():
         % (dec_steps, dec_ms * 1e3, dec_tok_s, dec_bw / 1e12, 100 * dec_bw / HBM_PEAK))
 
     # ---------------------------------------------------------------- prefill
-    prefill = None
-    if not args.no_prefill:
-        R = args.prefill_rows
+    def measure_prefill(R):
+        """Chunks of R rows rotating over the L layers (one Zipf offset per layer), replayed
+        from one HIP graph; returns the prefill record."""
         n_chunks = L
         zipf = [torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=i)).to(dev) for i in range(L)]
         xp = [torch.from_numpy(synth.make_x(shape, R, seed=2, stream=i, dtype="bf16")).view(torch.bfloat16).to(dev)
               for i in range(n_chunks)]
+        wsp = torch.empty(q.moe_workspace_bytes(shape, R), dtype=torch.uint8, device=dev)
+        q.moe_workspace_init(wsp)
         pidx = torch.empty(n_chunks, R, k, dtype=torch.int32, device=dev)
         pw = torch.empty(n_chunks, R, k, dtype=torch.float32, device=dev)
         cnt = torch.empty(n_chunks, E, dtype=torch.int32, device=dev)
@@ -235,7 +239,7 @@ def main():
 
         def prefill_step(i):
             q.moe_layer_prefill(shape, dls[i % L].c, xp[i], R, zipf[i % L], pidx[i], pw[i], cnt[i], off[i], perm[i],
-                                inv[i], peo, py[i], None, ws)
+                                inv[i], peo, py[i], None, wsp)
 
         for i in range(n_chunks):
             prefill_step(i)
@@ -250,18 +254,19 @@ def main():
         for _ in range(args.warmup):
             gp.replay()
         torch.cuda.synchronize()
-        ev0.record()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(p_replays):
             gp.replay()
-        ev1.record()
+        e1.record()
         torch.cuda.synchronize()
-        p_ms = ev0.elapsed_time(ev1) / (p_replays * n_chunks)
+        p_ms = e0.elapsed_time(e1) / (p_replays * n_chunks)
         ideal = [prefill_roofline(shape, counts[i], R) for i in range(n_chunks)]
         t_ideal = float(np.mean([t for t, _, _ in ideal]))
         flops = float(np.mean([fl for _, fl, _ in ideal]))
         nbytes = float(np.mean([by for _, _, by in ideal]))
         distinct = float(np.mean((counts > 0).sum(1)))
-        prefill = {
+        rec = {
             "workload": "prefill chunk of %d rows, same layer shape, Zipf(1.1)-skewed router logits" % R,
             "metric": "MoE-layer tokens/s (prefill chunk %d)" % R,
             "value": R / (p_ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": p_ms,
@@ -278,7 +283,16 @@ def main():
                                      zip(*np.unique(counts[counts > 0], return_counts=True))},
         }
         log("prefill: %d rows, %.1f us/chunk, %.0f tok/s, roofline frac %.3f, MFMA util %.3f, %.1f distinct experts"
-            % (R, p_ms * 1e3, prefill["value"], prefill["roofline"]["frac"], prefill["mfma_util"], distinct))
+            % (R, p_ms * 1e3, rec["value"], rec["roofline"]["frac"], rec["mfma_util"], distinct))
+        del gp
+        return rec
+
+    prefill = None
+    if not args.no_prefill:
+        prefill = measure_prefill(args.prefill_rows)
+    sweep = None
+    if args.sweep_chunks:
+        sweep = [measure_prefill(int(r)) for r in args.sweep_chunks.split(",")]
 
     # ---------------------------------------------------------------- 30-layer stacks
     stack = None
@@ -436,6 +450,8 @@ def main():
         "prefill": prefill,
         "stack": stack,
     }
+    if sweep is not None:
+        out["prefill_chunk_sweep"] = sweep
     print(json.dumps(out), flush=True)
 
 
