@@ -130,6 +130,10 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=128)
     ap.add_argument("--stack-rows", type=int, default=256, help="rows per chunk of the 30-layer prefill stack")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cache-slots", type=int, default=0,
+                    help="also decode through HBM expert slots per layer in front of a pinned host tier (0: off)")
+    ap.add_argument("--cache-layers", type=int, default=8, help="layers of the tiered-store decode leg")
+    ap.add_argument("--cache-tokens", type=int, default=40, help="timed tokens of the tiered-store decode leg")
     ap.add_argument("--sweep-chunks", default="", metavar="R1,R2,...",
                     help="also time prefill chunks of these row counts (reported under prefill_chunk_sweep)")
     ap.add_argument("--no-stack", action="store_true")
@@ -396,6 +400,72 @@ def main():
             % (NL, RS, sp_ms, stack["prefill"]["value"], stack["prefill"]["roofline"]["frac"],
                stack["prefill"]["mfma_util"]))
 
+    # ---------------------------------------------------------------- tiered residency (HBM slots + pinned host tier)
+    cache = None
+    if args.cache_slots > 0:
+        from quantized_mixture_experts_bit_amd.weights import HostExpertPool, TieredStore
+        NLc = min(args.cache_layers, L)
+        t0 = time.time()
+        host = HostExpertPool(shape, NLc)
+        for l in range(NLc):
+            host.load_layer(l, synth.make_layer(shape, seed=0, layer=l))
+        store = TieredStore(host, args.cache_slots, dev)
+        cl = [store.layer(l, dls[l].router, dls[l].shared) for l in range(NLc)]
+        log("tiered store: %d layers in pinned host memory (%.2f GB), %d HBM slots per layer, built in %.1f s"
+            % (NLc, host.buf.numel() / 1e9, args.cache_slots, time.time() - t0))
+        ws1 = torch.empty(q.moe_workspace_bytes(shape, 1), dtype=torch.uint8, device=dev)
+        q.moe_workspace_init(ws1)
+        cid, cw = torch.empty(k, dtype=torch.int32, device=dev), torch.empty(k, device=dev)
+        ceo, cy = torch.empty(k, d, device=dev), torch.empty(1, d, device=dev)
+        hc = torch.empty(1, d, dtype=torch.bfloat16, device=dev)
+        zoff = [torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=l)).to(dev) for l in range(NLc)]
+
+        def token(t, layers, offs, through_cache):
+            # one token through the NLc layers with the residual in place; the picks go to
+            # the host (a synchronising copy) when the experts come through the cache
+            hc.copy_(torch.from_numpy(synth.make_x(shape, 1, seed=500 + t, dtype="bf16")).view(torch.bfloat16))
+            for l in range(NLc):
+                q.moe_router_topk(shape, layers[l].c, hc, 1, offs[l], cid, cw, None, ws1)
+                if through_cache:
+                    layers[l].acquire(cid.cpu().numpy())
+                q.moe_expert_ffn_decode(shape, layers[l].c, hc, cid, ceo, ws1)
+                q.moe_combine(shape, layers[l].c, hc, 1, ceo, None, cw, cy, hc, ws1)
+
+        def timed(layers, offs, through_cache, n_tok, first):
+            for t in range(3):
+                token(first + t, layers, offs, through_cache)
+            torch.cuda.synchronize()
+            h0, m0, b0 = store.stats()
+            t0 = time.time()
+            for t in range(n_tok):
+                token(first + 3 + t, layers, offs, through_cache)
+            torch.cuda.synchronize()
+            dt = (time.time() - t0) / n_tok
+            h1, m1, b1 = store.stats()
+            hits, misses, nb = h1 - h0, m1 - m0, b1 - b0
+            return dt, hits, misses, nb
+
+        cache = {"workload": "decode, batch 1, %d-layer stack, residual in place; split calls (router, routed "
+                             "experts, shared + combine) with the picks copied to the host after each router; %d HBM "
+                             "expert slots per layer (LFU) in front of all %d x %d blobs in pinned host memory"
+                             % (NLc, args.cache_slots, NLc, E),
+                 "slots_per_layer": args.cache_slots, "layers": NLc}
+        n_tok = args.cache_tokens
+        for name, offs in (("uniform_router", [None] * NLc), ("zipf_router", zoff)):
+            dt_c, hits, misses, nb = timed(cl, offs, True, n_tok, 0 if name == "uniform_router" else 10000)
+            dt_r, _, _, _ = timed(dls, offs, False, n_tok, 0 if name == "uniform_router" else 10000)
+            rec = {"ms_per_token": dt_c * 1e3, "tokens_per_s": 1.0 / dt_c, "hit_rate": hits / max(1, hits + misses),
+                   "misses_per_token_layer": misses / (n_tok * NLc), "bytes_per_token": nb / n_tok,
+                   "host_to_hbm_GBps": nb / n_tok / dt_c / 1e9,
+                   "resident_ms_per_token": dt_r * 1e3, "slowdown_vs_resident": dt_c / dt_r, "tokens": n_tok}
+            cache[name] = rec
+            log("tiered decode (%s): %.2f ms/token (%.1f tok/s), hit rate %.3f, %.2f misses per token-layer, "
+                "%.1f MB/token from the host tier (%.1f GB/s), resident split path %.2f ms/token (%.2fx)"
+                % (name, rec["ms_per_token"], rec["tokens_per_s"], rec["hit_rate"], rec["misses_per_token_layer"],
+                   rec["bytes_per_token"] / 1e6, rec["host_to_hbm_GBps"], rec["resident_ms_per_token"],
+                   rec["slowdown_vs_resident"]))
+        store.close()
+
     # ---------------------------------------------------------------- CPU baseline (the oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -452,6 +522,8 @@ def main():
     }
     if sweep is not None:
         out["prefill_chunk_sweep"] = sweep
+    if cache is not None:
+        out["tiered_residency"] = cache
     print(json.dumps(out), flush=True)
 
 

@@ -224,6 +224,58 @@ moe_status moe_layer_prefill(const moe_shape* shape, const moe_layer* layer, con
                              float* expert_out, float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* ------------------------------------------------------------------ tiered expert residency */
+
+/*
+ * An HBM cache of expert blobs in front of a slower tier, per layer (the pages'
+ * per-layer 16-slot LFU cache with misses read in on demand: blog-mushroom
+ * article "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook", section "Why 26B
+ * Fits in 2 GB", per-token flow; paperfeed digest "drumih/turbo-fieldfare",
+ * "How it works"). The slow tier is pinned host memory.
+ *
+ * Memory, all owned by the caller:
+ *   host_pool     pinned host memory (e.g. hipHostMalloc, torch pin_memory):
+ *                 n_layers * n_experts blobs of blob_stride bytes, layer-major;
+ *                 blob (l, e) at host_pool + (l * n_experts + e) * blob_stride.
+ *   device_slots  device memory, n_layers * slots blobs: layer l's slots start at
+ *                 device_slots + l * slots * blob_stride.
+ *   slot_tables   device [n_layers][n_experts] uint32, kept up to date by the
+ *                 cache: the slot of each resident expert, `slots` for the others.
+ * Layer l then runs through a moe_layer with pool = its slots, n_blobs = slots and
+ * slot_table = slot_tables + l * n_experts, once its picks are resident.
+ *
+ * With device_slots and slot_tables both NULL the cache tracks the policy alone
+ * (no HIP calls; host_pool and blob_stride are ignored), for tests of the policy.
+ * moe_cache_create synchronises the device (it writes the initial tables); the
+ * cache's host state is allocated with new and pinned memory: it is the only
+ * allocation the library makes, and moe_cache_destroy frees it.
+ */
+typedef struct moe_expert_cache moe_expert_cache;
+
+moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t slots, uint64_t blob_stride,
+                            const uint8_t* host_pool, uint8_t* device_slots, uint32_t* slot_tables,
+                            moe_expert_cache** cache);
+
+/*
+ * Makes the experts idx_host[0..n) of `layer` resident (n <= slots; ids in range).
+ * Every request counts once toward its expert's frequency. A hit reuses the slot;
+ * a miss takes a never-used slot, else the slot of the resident expert with the
+ * smallest (frequency, last use, id) that this request does not name, and enqueues
+ * on `stream` the host-to-device copy of the blob and then of the layer's updated
+ * slot table. Kernels enqueued on the same stream afterwards see the experts in
+ * place; work enqueued earlier on it that used an evicted slot has run first.
+ * slot_host (nullable) [n] receives each request's slot, n_misses (nullable) the
+ * number of misses of this call. Host-side bookkeeping happens before return.
+ */
+moe_status moe_cache_acquire(moe_expert_cache* cache, int32_t layer, const int32_t* idx_host, int32_t n,
+                             int32_t* slot_host, int32_t* n_misses, void* stream);
+
+/* Totals since creation: requests that hit, requests that missed, bytes copied. */
+moe_status moe_cache_stats(const moe_expert_cache* cache, uint64_t* hits, uint64_t* misses, uint64_t* bytes_copied);
+
+/* Waits for the cache's own pending copies, then frees its host state. */
+moe_status moe_cache_destroy(moe_expert_cache* cache);
+
 /* ------------------------------------------------------------------ errors */
 
 const char* moe_status_string(moe_status status);

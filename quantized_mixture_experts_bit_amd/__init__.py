@@ -19,6 +19,7 @@ __all__ = [
     "moe_pack_matrix4", "moe_pack_matrix8", "moe_unpack_matrix4", "moe_unpack_matrix8",
     "moe_router_topk", "moe_group_by_expert", "moe_expert_ffn_decode", "moe_expert_ffn_prefill_chunk",
     "moe_combine", "moe_layer_decode", "moe_layer_prefill", "moe_status_string", "moe_check_device_error",
+    "moe_cache_create", "moe_cache_acquire", "moe_cache_stats", "moe_cache_destroy",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED_SHAPE", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_ERR_DEVICE_CHECK", "MOE_F32", "MOE_BF16", "MOE_DEVERR_BAD_SLOT",
 ]
@@ -96,6 +97,10 @@ def lib() -> C.CDLL:
                                        C.c_size_t, _P]),
             "moe_status_string": (C.c_char_p, [st]),
             "moe_check_device_error": (st, [_P, C.POINTER(C.c_uint32)]),
+            "moe_cache_create": (st, [i32, i32, i32, u64, _P, _P, _P, C.POINTER(_P)]),
+            "moe_cache_acquire": (st, [_P, i32, _P, i32, _P, _P, _P]),
+            "moe_cache_stats": (st, [_P, C.POINTER(u64), C.POINTER(u64), C.POINTER(u64)]),
+            "moe_cache_destroy": (st, [_P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -258,3 +263,47 @@ def moe_check_device_error(stream=None) -> int:
     if st not in (MOE_OK, MOE_ERR_DEVICE_CHECK):
         raise MoeError(st, "moe_check_device_error")
     return flags.value
+
+
+# ------------------------------------------------------------------ tiered expert residency
+
+def moe_cache_create(n_layers: int, n_experts: int, slots: int, blob_stride: int = 0, host_pool=None,
+                     device_slots=None, slot_tables=None) -> int:
+    """Returns the cache handle. host_pool: a pinned host torch uint8 tensor (or None);
+    device_slots, slot_tables: GPU tensors, or both None for the policy alone."""
+    h = C.c_void_p()
+    hp = None if host_pool is None else host_pool.data_ptr()
+    _check(lib().moe_cache_create(n_layers, n_experts, slots, blob_stride, hp, _dptr(device_slots),
+                                  _dptr(slot_tables), C.byref(h)), "moe_cache_create")
+    return h.value
+
+
+def moe_cache_acquire(cache: int, layer: int, idx, slots=None, stream=None) -> int:
+    """idx: host int32 numpy array of expert ids; slots: optional int32 numpy array that
+    receives their slots. Returns the number of misses."""
+    import numpy as np
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    miss = C.c_int32(0)
+    _check(lib().moe_cache_acquire(cache, layer, _hptr(idx), idx.size, None if slots is None else _hptr(slots),
+                                   C.byref(miss), _stream(stream) if stream is not None or _cuda_ok() else None),
+           "moe_cache_acquire")
+    return miss.value
+
+
+def moe_cache_stats(cache: int):
+    """(hits, misses, bytes copied) since creation."""
+    h, m, b = C.c_uint64(0), C.c_uint64(0), C.c_uint64(0)
+    _check(lib().moe_cache_stats(cache, C.byref(h), C.byref(m), C.byref(b)), "moe_cache_stats")
+    return h.value, m.value, b.value
+
+
+def moe_cache_destroy(cache: int) -> None:
+    _check(lib().moe_cache_destroy(cache), "moe_cache_destroy")
+
+
+def _cuda_ok() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except ImportError:
+        return False

@@ -1,0 +1,211 @@
+// Tiered expert residency (host side of the C ABI; no kernels).
+//
+// The pages keep every routed expert in the slow tier and, per layer, a 16-slot LFU
+// cache of expert blobs in GPU-visible memory: for each token the router's 8 picks are
+// looked up there, hits reuse the resident blob, misses are read in while the GPU runs
+// the shared expert, then both paths merge (blog-mushroom article "TurboFieldfare:
+// Gemma 4 26B on an 8 GB MacBook", section "Why 26B Fits in 2 GB", per-token flow;
+// paperfeed digest "drumih/turbo-fieldfare", "How it works"). Here the slow tier is
+// pinned host memory holding the blobs of every layer, the fast tier is `slots` HBM
+// blobs per layer, and the kernels reach a resident expert through the layer's slot
+// table (expert id -> slot), exactly as they reach the all-resident pool.
+//
+// Policy (per layer, deterministic): every request counts once toward its expert's
+// frequency; a missing expert takes a never-used slot if one is left, else the slot of
+// the resident expert with the smallest (frequency, last use, id) among those the
+// current request does not name. Slot-table entries of experts that are not resident
+// hold `slots` (outside the layer's pool), so a kernel that reached one would record a
+// bad-slot error instead of reading another expert's weights.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "moe.h"
+
+struct moe_expert_cache {
+  int32_t L = 0, E = 0, S = 0;
+  uint64_t stride = 0;
+  const uint8_t* host_pool = nullptr;  // [L][E] blobs, pinned host memory
+  uint8_t* dev_slots = nullptr;        // [L][S] blobs, device memory
+  uint32_t* dev_tables = nullptr;      // [L][E] device slot tables
+  bool host_only = false;              // no device side: the policy alone (for tests)
+  std::vector<uint32_t> freq;          // [L][E] requests so far
+  std::vector<int32_t> slot_of;        // [L][E] slot or -1
+  std::vector<int32_t> expert_in;      // [L][S] expert or -1
+  std::vector<uint64_t> last_use;      // [L][S] request counter at the last use
+  uint64_t clock = 0;
+  uint32_t* table_stage = nullptr;     // [L][E] pinned host copy of the slot tables
+  std::vector<hipEvent_t> staged;      // [L] the last table copy of each layer
+  std::vector<bool> staged_live;
+  uint64_t hits = 0, misses = 0, bytes = 0;
+};
+
+namespace {
+
+moe_status hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+void release(moe_expert_cache* c) {
+  if (!c) return;
+  for (size_t l = 0; l < c->staged.size(); ++l)
+    if (c->staged_live[l]) (void)hipEventDestroy(c->staged[l]);
+  if (c->table_stage) (void)hipHostFree(c->table_stage);
+  delete c;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t slots, uint64_t blob_stride,
+                            const uint8_t* host_pool, uint8_t* device_slots, uint32_t* slot_tables,
+                            moe_expert_cache** cache) {
+  if (!cache) return MOE_ERR_INVALID_ARG;
+  *cache = nullptr;
+  if (n_layers < 1 || n_experts < 1 || n_experts > 256 || slots < 1 || slots > n_experts) return MOE_ERR_INVALID_ARG;
+  const bool host_only = device_slots == nullptr && slot_tables == nullptr;
+  if (!host_only && (!device_slots || !slot_tables || !host_pool || blob_stride == 0 || blob_stride % 256))
+    return MOE_ERR_INVALID_ARG;
+  moe_expert_cache* c = new (std::nothrow) moe_expert_cache;
+  if (!c) return MOE_ERR_INVALID_ARG;
+  c->L = n_layers;
+  c->E = n_experts;
+  c->S = slots;
+  c->stride = blob_stride;
+  c->host_pool = host_pool;
+  c->dev_slots = device_slots;
+  c->dev_tables = slot_tables;
+  c->host_only = host_only;
+  const size_t LE = (size_t)n_layers * n_experts, LS = (size_t)n_layers * slots;
+  c->freq.assign(LE, 0u);
+  c->slot_of.assign(LE, -1);
+  c->expert_in.assign(LS, -1);
+  c->last_use.assign(LS, 0u);
+  c->staged.resize(n_layers);
+  c->staged_live.assign(n_layers, false);
+  if (!host_only) {
+    // nothing resident: every entry points past the layer's slots (synchronous)
+    if (hipHostMalloc((void**)&c->table_stage, LE * sizeof(uint32_t), hipHostMallocDefault) != hipSuccess) {
+      c->table_stage = nullptr;
+      release(c);
+      return MOE_ERR_HIP;
+    }
+    for (size_t i = 0; i < LE; ++i) c->table_stage[i] = (uint32_t)slots;
+    for (int32_t l = 0; l < n_layers; ++l) {
+      if (hipEventCreateWithFlags(&c->staged[l], hipEventDisableTiming) != hipSuccess) {
+        release(c);
+        return MOE_ERR_HIP;
+      }
+      c->staged_live[l] = true;
+    }
+    if (hipMemcpy(slot_tables, c->table_stage, LE * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) {
+      release(c);
+      return MOE_ERR_HIP;
+    }
+  }
+  *cache = c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_acquire(moe_expert_cache* c, int32_t layer, const int32_t* idx_host, int32_t n,
+                             int32_t* slot_host, int32_t* n_misses, void* stream) {
+  if (!c || !idx_host || layer < 0 || layer >= c->L || n < 1 || n > c->S) return MOE_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (idx_host[i] < 0 || idx_host[i] >= c->E) return MOE_ERR_INVALID_ARG;
+  const size_t le = (size_t)layer * c->E, ls = (size_t)layer * c->S;
+  uint32_t* freq = c->freq.data() + le;
+  int32_t* slot_of = c->slot_of.data() + le;
+  int32_t* expert_in = c->expert_in.data() + ls;
+  uint64_t* last_use = c->last_use.data() + ls;
+  hipStream_t st = (hipStream_t)stream;
+
+  // the staging copy of this layer's table is rewritten below: its previous upload must be done
+  if (!c->host_only && hipEventSynchronize(c->staged[layer]) != hipSuccess) return MOE_ERR_HIP;
+
+  const uint64_t now = ++c->clock;
+  std::vector<bool> named(c->E, false);
+  for (int32_t i = 0; i < n; ++i) {
+    if (!named[idx_host[i]]) ++freq[idx_host[i]];
+    named[idx_host[i]] = true;
+  }
+  int32_t miss = 0;
+  bool table_changed = false;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t e = idx_host[i];
+    int32_t s = slot_of[e];
+    if (s >= 0) {
+      ++c->hits;
+    } else {
+      // a never-used slot, else the least-frequently used resident the request does not name
+      s = -1;
+      for (int32_t j = 0; j < c->S && s < 0; ++j)
+        if (expert_in[j] < 0) s = j;
+      if (s < 0) {
+        for (int32_t j = 0; j < c->S; ++j) {
+          const int32_t v = expert_in[j];
+          if (named[v]) continue;
+          if (s < 0) {
+            s = j;
+            continue;
+          }
+          const int32_t w = expert_in[s];
+          if (freq[v] < freq[w] || (freq[v] == freq[w] && (last_use[j] < last_use[s] ||
+                                                           (last_use[j] == last_use[s] && v < w))))
+            s = j;
+        }
+      }
+      if (s < 0) return MOE_ERR_INVALID_ARG;  // unreachable: n <= slots
+      if (expert_in[s] >= 0) {
+        slot_of[expert_in[s]] = -1;
+        if (!c->host_only) c->table_stage[le + expert_in[s]] = (uint32_t)c->S;
+      }
+      expert_in[s] = e;
+      slot_of[e] = s;
+      if (!c->host_only) {
+        c->table_stage[le + e] = (uint32_t)s;
+        if (hipMemcpyAsync(c->dev_slots + (ls + s) * c->stride, c->host_pool + (le + e) * c->stride, c->stride,
+                           hipMemcpyHostToDevice, st) != hipSuccess)
+          return MOE_ERR_HIP;
+        c->bytes += c->stride;
+      }
+      table_changed = true;
+      ++c->misses;
+      ++miss;
+    }
+    last_use[s] = now;
+    if (slot_host) slot_host[i] = s;
+  }
+  if (!c->host_only && table_changed) {
+    if (hipMemcpyAsync(c->dev_tables + le, c->table_stage + le, (size_t)c->E * sizeof(uint32_t),
+                       hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipEventRecord(c->staged[layer], st) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (n_misses) *n_misses = miss;
+  return MOE_OK;
+}
+
+moe_status moe_cache_stats(const moe_expert_cache* c, uint64_t* hits, uint64_t* misses, uint64_t* bytes_copied) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (hits) *hits = c->hits;
+  if (misses) *misses = c->misses;
+  if (bytes_copied) *bytes_copied = c->bytes;
+  return MOE_OK;
+}
+
+moe_status moe_cache_destroy(moe_expert_cache* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (!c->host_only)
+    for (int32_t l = 0; l < c->L; ++l)
+      if (c->staged_live[l] && hipEventSynchronize(c->staged[l]) != hipSuccess) {
+        release(c);
+        return MOE_ERR_HIP;
+      }
+  release(c);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -19,7 +19,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (as_shape, moe_expert_blob_bytes, moe_layer, moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4,
+from . import (as_shape, moe_cache_acquire, moe_cache_create, moe_cache_destroy, moe_cache_stats,
+               moe_expert_blob_bytes, moe_layer, moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4,
                moe_pack_matrix8, moe_router_blob_bytes, moe_shared_blob_bytes)
 
 BLOB_ALIGN = 4096  # blob stride granularity (a page)
@@ -111,3 +112,66 @@ def upload_layers(shape, layers: List, device="cuda") -> List[DeviceLayer]:
     E = shape.n_experts
     pool = ExpertPool(shape, len(layers) * E, device)
     return [pool.add_layer(L, i * E) for i, L in enumerate(layers)]
+
+
+# ------------------------------------------------------------------ tiered residency
+
+class HostExpertPool:
+    """Slow tier: every expert blob of `n_layers` layers in pinned host memory,
+    layer-major (blob (l, e) at (l * n_experts + e) * stride)."""
+
+    def __init__(self, shape, n_layers: int, stride: Optional[int] = None):
+        blob = moe_expert_blob_bytes(as_shape(shape))
+        self.shape = shape
+        self.n_layers = n_layers
+        self.stride = stride or (blob + BLOB_ALIGN - 1) // BLOB_ALIGN * BLOB_ALIGN
+        self.buf = torch.empty(n_layers * shape.n_experts * self.stride, dtype=torch.uint8, pin_memory=True)
+
+    def load_layer(self, l: int, layer) -> None:
+        E = self.shape.n_experts
+        host = self.buf.numpy()
+        base = l * E * self.stride
+        with cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(lambda e: pack_expert_into(self.shape, layer.experts[e],
+                                                   host[base + e * self.stride:base + (e + 1) * self.stride]),
+                        range(E)))
+
+
+class CachedLayer:
+    """One layer of a TieredStore as the C ABI sees it (`c`): its HBM slots as the
+    pool, its slot table, and the resident router and shared blobs."""
+
+    def __init__(self, store: "TieredStore", l: int, router: torch.Tensor, shared: torch.Tensor):
+        self.store, self.l, self.router, self.shared = store, l, router, shared
+        S, st = store.slots, store.stride
+        self.c = moe_layer(store.dev_slots.data_ptr() + l * S * st, st, S,
+                           store.tables.data_ptr() + l * store.shape.n_experts * 4, router.data_ptr(),
+                           shared.data_ptr())
+
+    def acquire(self, idx, slots=None, stream=None) -> int:
+        """Makes the experts idx (host int32 array) resident; returns the misses."""
+        return moe_cache_acquire(self.store.handle, self.l, idx, slots, stream)
+
+
+class TieredStore:
+    """Fast tier: `slots` HBM expert slots per layer in front of a HostExpertPool,
+    managed by the library's cache (moe_cache_*)."""
+
+    def __init__(self, host: HostExpertPool, slots: int, device="cuda"):
+        self.shape, self.host, self.slots, self.stride = host.shape, host, slots, host.stride
+        E, L = host.shape.n_experts, host.n_layers
+        dev = torch.device(device)
+        self.dev_slots = torch.empty(L * slots * self.stride, dtype=torch.uint8, device=dev)
+        self.tables = torch.empty(L * E, dtype=torch.int32, device=dev)
+        self.handle = moe_cache_create(L, E, slots, self.stride, host.buf, self.dev_slots, self.tables)
+
+    def layer(self, l: int, router: torch.Tensor, shared: torch.Tensor) -> CachedLayer:
+        return CachedLayer(self, l, router, shared)
+
+    def stats(self):
+        return moe_cache_stats(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            moe_cache_destroy(self.handle)
+            self.handle = None

@@ -1,0 +1,122 @@
+"""Host-side policy of the tiered expert cache (moe_cache_*, policy-only mode: no device
+side, no HIP calls), against a model of the rule written here from its statement in
+include/moe.h: every request counts once toward its expert's frequency; a miss takes a
+never-used slot if one is left, else the slot of the resident expert with the smallest
+(frequency, last use, id) that the current request does not name."""
+import numpy as np
+import pytest
+
+q = pytest.importorskip("quantized_mixture_experts_bit_amd")
+
+
+class LfuModel:
+    def __init__(self, n_layers, n_experts, slots):
+        self.S = slots
+        self.freq = [[0] * n_experts for _ in range(n_layers)]
+        self.slot_of = [dict() for _ in range(n_layers)]      # expert -> slot
+        self.expert_in = [[None] * slots for _ in range(n_layers)]
+        self.last = [[0] * slots for _ in range(n_layers)]
+        self.clock = 0
+        self.hits = self.misses = 0
+
+    def acquire(self, layer, idx):
+        self.clock += 1
+        named = set(idx)
+        for e in named:
+            self.freq[layer][e] += 1
+        out, miss = [], 0
+        for e in idx:
+            s = self.slot_of[layer].get(e)
+            if s is not None:
+                self.hits += 1
+            else:
+                free = [j for j in range(self.S) if self.expert_in[layer][j] is None]
+                if free:
+                    s = free[0]
+                else:
+                    cands = [j for j in range(self.S) if self.expert_in[layer][j] not in named]
+                    s = min(cands, key=lambda j: (self.freq[layer][self.expert_in[layer][j]], self.last[layer][j],
+                                                  self.expert_in[layer][j]))
+                    del self.slot_of[layer][self.expert_in[layer][s]]
+                self.expert_in[layer][s] = e
+                self.slot_of[layer][e] = s
+                self.misses += 1
+                miss += 1
+            self.last[layer][s] = self.clock
+            out.append(s)
+        return out, miss
+
+
+def run_both(n_layers, E, S, requests):
+    h = q.moe_cache_create(n_layers, E, S)
+    m = LfuModel(n_layers, E, S)
+    try:
+        for layer, idx in requests:
+            idx = np.asarray(idx, dtype=np.int32)
+            slots = np.empty(idx.size, dtype=np.int32)
+            miss = q.moe_cache_acquire(h, layer, idx, slots)
+            want, want_miss = m.acquire(layer, [int(v) for v in idx])
+            assert slots.tolist() == want, (layer, idx.tolist())
+            assert miss == want_miss
+        hits, misses, nbytes = q.moe_cache_stats(h)
+        assert (hits, misses) == (m.hits, m.misses)
+        assert nbytes == 0  # policy-only: nothing copied
+    finally:
+        q.moe_cache_destroy(h)
+    return m
+
+
+def test_first_requests_fill_slots_in_order():
+    m = run_both(1, 128, 16, [(0, [5, 9, 1, 7]), (0, [2, 5, 11, 13])])
+    assert m.slot_of[0] == {5: 0, 9: 1, 1: 2, 7: 3, 2: 4, 11: 5, 13: 6}
+    assert (m.hits, m.misses) == (1, 7)
+
+
+def test_least_frequent_is_evicted_and_ties_go_to_least_recent_then_lowest_id():
+    # four slots; expert 1 is requested twice, 2 and 3 once each (3 more recently than 2)
+    reqs = [(0, [0, 1]), (0, [2, 1]), (0, [3]), (0, [4])]
+    m = run_both(1, 64, 4, reqs)
+    # slots: 0->expert 0, 1->1, 2->2, 3->3, then 4 evicts the lowest (freq, last use): expert 0 (freq 1, clock 1)
+    assert m.slot_of[0].get(4) == 0 and 0 not in m.slot_of[0]
+    # a tie on frequency and last use goes to the lower id
+    m2 = run_both(1, 64, 2, [(0, [7, 3]), (0, [9])])
+    assert m2.slot_of[0] == {7: 0, 9: 1}
+
+
+def test_named_experts_are_never_evicted_and_duplicates_count_once():
+    m = run_both(1, 64, 3, [(0, [1, 2, 3]), (0, [1, 1, 4]), (0, [2, 5, 4])])
+    assert m.freq[0][1] == 2
+    for e in (2, 5, 4):
+        assert e in m.slot_of[0]
+
+
+@pytest.mark.parametrize("n_layers,E,S,k,skew", [(3, 128, 16, 8, 1.1), (2, 256, 16, 16, 0.0), (1, 64, 8, 4, 2.0),
+                                                  (4, 128, 8, 8, 1.1)])
+def test_random_streams_match_the_model(n_layers, E, S, k, skew):
+    rng = np.random.default_rng(E * 7 + S + k)
+    p = 1.0 / np.arange(1, E + 1) ** skew
+    p /= p.sum()
+    perm = [rng.permutation(E) for _ in range(n_layers)]
+    reqs = []
+    for _ in range(400):
+        layer = int(rng.integers(n_layers))
+        picks = perm[layer][rng.choice(E, size=k, replace=False, p=p)]
+        reqs.append((layer, picks.tolist()))
+    m = run_both(n_layers, E, S, reqs)
+    if skew > 1.0 and S >= 2 * k:
+        assert m.hits > m.misses  # skewed routing reuses experts when the cache holds two requests
+
+
+def test_invalid_requests_are_rejected():
+    h = q.moe_cache_create(2, 64, 4)
+    try:
+        for layer, idx in [(2, [1]), (-1, [1]), (0, [64]), (0, [-1]), (0, [1, 2, 3, 4, 5])]:
+            with pytest.raises(q.MoeError):
+                q.moe_cache_acquire(h, layer, np.asarray(idx, dtype=np.int32))
+        with pytest.raises(q.MoeError):
+            q.moe_cache_acquire(h, 0, np.zeros(0, dtype=np.int32))
+    finally:
+        q.moe_cache_destroy(h)
+    for args in [(0, 64, 4), (1, 64, 0), (1, 64, 65), (1, 0, 1), (1, 300, 4)]:
+        with pytest.raises(q.MoeError):
+            q.moe_cache_create(*args)
