@@ -96,6 +96,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Maximum over the 16 lanes of each DPP row (lanes 16q .. 16q + 15), returned to every
+// lane of the row: the first four steps of wave_sum with fmaxf in place of add (so a
+// NaN is skipped, as fmaxf does).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf,
+                                                                        0xf, false)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_fmax<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_fmax<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_fmax<0x141>(v);  // row_half_mirror
+  return dpp_fmax<0x140>(v);  // row_mirror
+}
+
 // Maximum over the 64 lanes of a wavefront (unsigned), returned to every lane: the
 // DPP steps of wave_sum with max in place of add (rows outside a step's row mask keep
 // their value: the moved-in 0 is the identity of max on unsigned values).

@@ -424,10 +424,8 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
           h = gelu_tanh(acc[mb][0][i]) * acc[mb][1][i];
           H[(size_t)(T.m0 + r) * F + fc * 64 + 16 * wave + (lane & 15)] = h;
         }
-        // max |h| over the 16 lanes holding this row
-        float mx = fabsf(h);
-  #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        // max |h| over the 16 lanes holding this row: one DPP row (VALU, no LDS round trips)
+        const float mx = row16_max(fabsf(h));
         if ((lane & 15) == 0) hmL[wave][r] = mx;
       }
     __syncthreads();
