@@ -71,10 +71,14 @@ struct NibKT {
 };
 using NibK = NibKT<>;
 
-// tanh form of GELU (Hendrycks & Gimpel), fp32
+// tanh form of GELU (Hendrycks & Gimpel), fp32: 0.5 z (1 + tanh u) with
+// u = sqrt(2/pi) (z + 0.044715 z^3), evaluated as z / (1 + exp(-2u)) (the same
+// function: (1 + tanh u) / 2 is the logistic function of 2u) with the hardware
+// exp2 and a division; z -> -inf gives z / inf = 0 and z -> +inf gives z.
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+  const float c2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float t = exp2f(c2 * (z + 0.044715f * z * z * z));
+  return z / (1.0f + t);
 }
 
 // Sum over the 64 lanes of a wavefront, returned to every lane. DPP row operations
