@@ -327,7 +327,8 @@ void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, hipStr
   const int first = routed ? 0 : P;
   const int count = (routed ? P : 0) + (shared ? A.rows : 0);
   k_prefill_hconv<<<cdiv(count, 4), 256, 0, st>>>(A, first, count);
-  const int dn_items = xcd_blocks(A.routed_mtiles, A.d / 64) + xcd_blocks(A.shared_mtiles, A.d / 64);
+  const int dnc = (A.d / 64 + kDownBlocks - 1) / kDownBlocks;
+  const int dn_items = xcd_blocks(A.routed_mtiles, dnc) + xcd_blocks(A.shared_mtiles, dnc);
   k_prefill_down<<<persistent_grid(resident_blocks(k_prefill_down, cap_dn), dn_items), 256, 0, st>>>(A);
 }
 

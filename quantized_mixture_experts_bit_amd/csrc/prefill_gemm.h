@@ -516,9 +516,12 @@ struct DownSmem {
   float rowinv[64];
 };
 
-// One work item = (64-row tile, 64 output columns). Wave w owns output columns
-// [16w, +16) for every row of the tile.
-__device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, int nb, bool shared, DownSmem& S) {
+// One work item = (64-row tile, two blocks of 64 output columns, 2 np and 2 np + 1).
+// Wave w owns output columns [16w, +16) of both blocks for every row of the tile, so
+// one staged H tile feeds twice the columns. With an odd number of blocks the last
+// item's second block repeats its first and is not stored.
+constexpr int kDownBlocks = 2;
+__device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, int np, bool shared, DownSmem& S) {
   constexpr int RA = 4;
   auto& Hl = S.Hl;
   auto& rowinv = S.rowinv;
@@ -531,9 +534,16 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   const float* hsc = shared ? A.hsc + P : A.hsc;
 
   const int wrow = 16 * wave + (lane & 15);
-  const rsrc_t wres[1] = {
-      buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nb * G * kTile4, (uint32_t)G * kTile4)};
-  BRing<1> B;
+  const int nblk = A.d / 64;
+  int nbm[kDownBlocks];
+  rsrc_t wres[kDownBlocks];
+#pragma unroll
+  for (int m = 0; m < kDownBlocks; ++m) {
+    nbm[m] = min(kDownBlocks * np + m, nblk - 1);
+    wres[m] = buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nbm[m] * G * kTile4,
+                       (uint32_t)G * kTile4);
+  }
+  BRing<kDownBlocks> B;
   B.init(wrow, lane);
   if (tid < 64) rowinv[tid] = tid < T.mrows ? 1.0f / hsc[T.m0 + tid] : 1.0f;  // exact: powers of two
 
@@ -569,9 +579,11 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   });
   __syncthreads();
 
-  f32x4_t acc[4];
+  f32x4_t acc[4][kDownBlocks];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) zero_acc(acc[mb]);
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int m = 0; m < kDownBlocks; ++m) zero_acc(acc[mb][m]);
   const f16x8_t ones = __builtin_bit_cast(f16x8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
   // one K group, as in the gate/up kernel
@@ -579,10 +591,15 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   auto step = [&](auto jc, int g) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     constexpr int buf = j & 1;
-    const f16x8_t b0 = codes_f16(B.cw[j][0][0], nk);
-    const f16x8_t b1 = codes_f16(B.cw[j][0][1], nk);
-    const float s = bf16_lo(B.sb[j][0]);
-    const float bp = bf16_hi(B.sb[j][0]);
+    f16x8_t b0[kDownBlocks], b1[kDownBlocks];
+    float s[kDownBlocks], bp[kDownBlocks];
+#pragma unroll
+    for (int m = 0; m < kDownBlocks; ++m) {
+      b0[m] = codes_f16(B.cw[j][m][0], nk);
+      b1[m] = codes_f16(B.cw[j][m][1], nk);
+      s[m] = bf16_lo(B.sb[j][m]);
+      bp[m] = bf16_hi(B.sb[j][m]);
+    }
     B.load(jc, wres, min(g + kRing, G - 1));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -591,9 +608,12 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
         const f16x8_t a0 = lds_frag<f16x8_t>(&Hl[buf][ao]);
         const f16x8_t a1 = lds_frag<f16x8_t>(&Hl[buf][ao + 32]);
         const f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
-        const f32x4_t t = mfma(a1, b1, mfma(a0, b0, f32x4_t{0.f, 0.f, 0.f, 0.f}));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(s, t[i], fmaf(bp, ag[i], acc[mb][i]));
+        for (int m = 0; m < kDownBlocks; ++m) {
+          const f32x4_t t = mfma(a1, b1[m], mfma(a0, b0[m], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[i], fmaf(bp[m], ag[i], acc[mb][m][i]));
+        }
       }
     }
     astore(ic<(j + 1) % RA>{}, buf ^ 1);
@@ -612,12 +632,17 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
   float* out = shared ? A.shared_out : A.expert_out;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int m = 0; m < kDownBlocks; ++m) {
+    if (kDownBlocks * np + m >= nblk) break;  // the repeated last block
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mb + 4 * (lane >> 4) + i;
-      if (r < T.mrows) out[(size_t)(T.m0 + r) * A.d + nb * 64 + 16 * wave + (lane & 15)] = acc[mb][i] * rowinv[r];
-    }
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mb + 4 * (lane >> 4) + i;
+        if (r < T.mrows)
+          out[(size_t)(T.m0 + r) * A.d + nbm[m] * 64 + 16 * wave + (lane & 15)] = acc[mb][m][i] * rowinv[r];
+      }
+  }
 }
 
 // Persistent over the work items, as the gate/up kernel.
@@ -625,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_down(PrefillArgs A) {
   __shared__ DownSmem S;
   TileMap M;
   const int nrt = A.routed_mtiles > 0 ? tile_map_init(A, M) : 0;
-  const int nc = A.d / 64;
+  const int nc = (A.d / 64 + kDownBlocks - 1) / kDownBlocks;
   const int ns = xcd_blocks(A.shared_mtiles, nc);
   const int n = ns + xcd_blocks(nrt, nc);
   for (int item = blockIdx.x; item < n; item += gridDim.x) {
