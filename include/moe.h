@@ -197,7 +197,9 @@ moe_status moe_expert_ffn_prefill_chunk(const moe_shape* shape, const moe_layer*
  * bf16 [rows][d_model] in/out buffer: residual = bf16_rne(fp32(residual) + y)
  * (the residual add between stacked layers). It may be the buffer x itself
  * (bf16 x): every read of x precedes the residual store, here and in the
- * fused layer calls below.
+ * fused layer calls below. expert_out and y must be 16-byte aligned and
+ * residual_bf16 8-byte aligned (MOE_ERR_INVALID_ARG otherwise; rows of
+ * d_model elements keep every row aligned).
  */
 moe_status moe_combine(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                        int32_t rows, const float* expert_out, const int32_t* inv_perm, const float* topk_w,
@@ -216,7 +218,8 @@ moe_status moe_layer_decode(const moe_shape* shape, const moe_layer* layer, cons
 /*
  * Whole block for a prefill chunk: router + top-k, grouping, grouped expert
  * GEMMs, shared expert and combine (+ optional residual). Outputs as the
- * separate calls; count/offset/perm/inv_perm as moe_group_by_expert.
+ * separate calls (with the alignment moe_combine asks for);
+ * count/offset/perm/inv_perm as moe_group_by_expert.
  */
 moe_status moe_layer_prefill(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                              int32_t rows, const float* logit_offset, int32_t* topk_idx, float* topk_w,

@@ -120,25 +120,46 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ topk
 }
 
 // y[r][n] = S[r][n] + sum_k w[r][k] * E[pos(r, k)][n], k in slot order; optional residual
-// x' = bf16_rne(fp32(x) + y).
+// x' = bf16_rne(fp32(x) + y). Workgroup (column block, row r): four consecutive columns
+// per thread; the row's positions and weights are uniform, and every routed output of
+// the thread is loaded before the first one is added (top_k <= kMaxTopK).
+constexpr int kMaxTopK = 16;
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ shared_out,
                                                  const float* __restrict__ expert_out,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ topk_w, int rows, int d, int top_k,
                                                  float* __restrict__ y, uint16_t* __restrict__ residual) {
   const int r = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int n = 4 * ((int)blockIdx.x * 256 + (int)threadIdx.x);
   if (n >= d) return;
-  float v = shared_out[(size_t)r * d + n];
-  for (int k = 0; k < top_k; ++k) {
-    const int pos = inv_perm ? inv_perm[r * top_k + k] : r * top_k + k;
-    if (pos < 0) continue;  // a pair the grouping dropped (invalid id, already reported)
-    v = fmaf(topk_w[r * top_k + k], expert_out[(size_t)pos * d + n], v);
+  int pos[kMaxTopK];
+  float4 e[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k < top_k) {
+      pos[k] = inv_perm ? inv_perm[r * top_k + k] : r * top_k + k;
+      // a pair the grouping dropped (invalid id, already reported) has no output
+      e[k] = *reinterpret_cast<const float4*>(expert_out + (size_t)max(pos[k], 0) * d + n);
+    }
   }
-  y[(size_t)r * d + n] = v;
+  float4 v = *reinterpret_cast<const float4*>(shared_out + (size_t)r * d + n);
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k < top_k && pos[k] >= 0) {
+      const float w = topk_w[r * top_k + k];
+      v.x = fmaf(w, e[k].x, v.x);
+      v.y = fmaf(w, e[k].y, v.y);
+      v.z = fmaf(w, e[k].z, v.z);
+      v.w = fmaf(w, e[k].w, v.w);
+    }
+  }
+  *reinterpret_cast<float4*>(y + (size_t)r * d + n) = v;
   if (residual) {
-    const float t = bf16_to_f32(residual[(size_t)r * d + n]) + v;
-    residual[(size_t)r * d + n] = (uint16_t)f32_to_bf16_bits(t);
+    const uint2 rb = *reinterpret_cast<const uint2*>(residual + (size_t)r * d + n);
+    const float t0 = bf16_lo(rb.x) + v.x, t1 = bf16_hi(rb.x) + v.y;
+    const float t2 = bf16_lo(rb.y) + v.z, t3 = bf16_hi(rb.y) + v.w;
+    *reinterpret_cast<uint2*>(residual + (size_t)r * d + n) =
+        make_uint2(f32_to_bf16_bits(t0) | (f32_to_bf16_bits(t1) << 16), f32_to_bf16_bits(t2) | (f32_to_bf16_bits(t3) << 16));
   }
 }
 

@@ -431,6 +431,7 @@ moe_status moe_combine(const moe_shape* s, const moe_layer* L, const void* x, mo
   if ((st = check_layer(s, L, false, false, true)) != MOE_OK) return st;
   if (rows == 0) return MOE_OK;
   if (!expert_out || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(expert_out) || !aligned16(y) || ((uintptr_t)residual & 7u)) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
   if (rows == 1 && inv_perm == nullptr) {
     // decode: shared expert as GEMVs, the combine runs in the last workgroup of each output block
@@ -447,7 +448,7 @@ moe_status moe_combine(const moe_shape* s, const moe_layer* L, const void* x, mo
     launch_prefill(A, (const uint16_t*)x, false, true, hs);
   else
     launch_prefill(A, (const float*)x, false, true, hs);
-  k_combine<<<dim3(cdiv(s->d_model, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, topk_w, rows,
+  k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, topk_w, rows,
                                                                  s->d_model, s->top_k, y, residual);
   return launched();
 }
@@ -486,6 +487,7 @@ moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void*
   if ((st = check_layer(s, L, true, true, true)) != MOE_OK) return st;
   if (rows == 0) return MOE_OK;
   if (!idx || !w || !count || !offset || !perm || !inv_perm || !expert_out || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(expert_out) || !aligned16(y) || ((uintptr_t)residual & 7u)) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
   if (dt == MOE_BF16)
     launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, nullptr, ws, hs);
@@ -498,7 +500,7 @@ moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void*
     launch_prefill(A, (const uint16_t*)x, true, true, hs);
   else
     launch_prefill(A, (const float*)x, true, true, hs);
-  k_combine<<<dim3(cdiv(s->d_model, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, w, rows,
+  k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, w, rows,
                                                                  s->d_model, s->top_k, y, residual);
   return launched();
 }

@@ -472,8 +472,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill_gateup(PrefillArgs A, const 
 // ---------------------------------------------------------------- H to fp16
 
 // One wavefront per H row (rows [first, first + count) of the routed rows followed
-// by the shared rows): the row's power-of-two scale from its per-block maxima,
-// then the fp16 copy of h * scale.
+// by the shared rows): the row's power-of-two scale from its per-block maxima, then
+// the fp16 copy of h * scale. Every load of a round (the maxima and up to
+// kHconvLoads 16-byte pieces of the row per lane) is issued before any is used.
+constexpr int kHconvLoads = 8;
 __global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first, int count) {
   const int lane = threadIdx.x & 63;
   const int r = first + (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
@@ -495,17 +497,35 @@ __global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first,
     mp = A.hmaxp + (size_t)P * (A.f / 64) + (size_t)rs * (F / 64);
     dst = A.Hh + (size_t)P * A.f + (size_t)rs * F;
   }
+  const int nG = F / 64;
+  const rsrc_t hres = buf_rsrc(src, (uint32_t)F * 4u);  // loads past the row return 0
   float m = 0.0f;
-  for (int i = lane; i < F / 64; i += 64) m = fmaxf(m, mp[i]);
+  for (int c0 = 0; c0 < F; c0 += 256 * kHconvLoads) {
+    u32x4_t v[kHconvLoads];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  const float sc = row_scale(m);
-  if (lane == 0) A.hsc[r] = sc;
-  for (int c = 4 * lane; c < F; c += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(src + c);
-    const uint32_t p0 = (uint32_t)f16_bits(v.x * sc) | ((uint32_t)f16_bits(v.y * sc) << 16);
-    const uint32_t p1 = (uint32_t)f16_bits(v.z * sc) | ((uint32_t)f16_bits(v.w * sc) << 16);
-    *reinterpret_cast<uint2*>(dst + c) = make_uint2(p0, p1);
+    for (int j = 0; j < kHconvLoads; ++j) v[j] = bld16(hres, (uint32_t)(c0 + 256 * j + 4 * lane) * 4u, 0);
+    if (c0 == 0) {
+      for (int i = lane; i < nG; i += 64) m = fmaxf(m, mp[i]);
+      // fmaxf over the wavefront (a NaN maximum is skipped, as fmaxf does)
+      m = row16_max(m);
+      m = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0)),
+                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16))),
+                fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32)),
+                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48))));
+    }
+    const float sc = row_scale(m);
+    if (c0 == 0 && lane == 0) A.hsc[r] = sc;
+#pragma unroll
+    for (int j = 0; j < kHconvLoads; ++j) {
+      const int c = c0 + 256 * j + 4 * lane;
+      if (c < F) {
+        const uint32_t p0 = (uint32_t)f16_bits(__uint_as_float(v[j][0]) * sc) |
+                            ((uint32_t)f16_bits(__uint_as_float(v[j][1]) * sc) << 16);
+        const uint32_t p1 = (uint32_t)f16_bits(__uint_as_float(v[j][2]) * sc) |
+                            ((uint32_t)f16_bits(__uint_as_float(v[j][3]) * sc) << 16);
+        *reinterpret_cast<uint2*>(dst + c) = make_uint2(p0, p1);
+      }
+    }
   }
 }
 

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_router_select(const double* __restrict_
     const int se = lane < top_k ? sel_e[lane] : 0;
     const double ex = lane < top_k ? exp(lgv[se] - lgv[sel_e[0]]) : 0.0;
     double sum = 0.0;
-    for (int t = 0; t < top_k; ++t) sum += __shfl(ex, t, 64);
+    for (int t = 0; t < top_k; ++t) sum += readlane_f64(ex, t);
     if (lane < top_k) {
       topk_idx[(size_t)row * top_k + lane] = se;
       topk_w[(size_t)row * top_k + lane] = (float)(ex / sum);

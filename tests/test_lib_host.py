@@ -142,6 +142,26 @@ def test_invalid_pool_is_rejected():
     assert st == q.MOE_ERR_INVALID_ARG
 
 
+def test_misaligned_combine_buffers_are_rejected():
+    # expert_out and y are read and written four floats at a time, the residual four bf16 at a time
+    lib = q.lib()
+    s = q.MoeShape(2816, 704, 2112)
+    L = C.byref(_fake_layer())
+
+    def combine(eo=0x60000, y=0x90000, res=None):
+        return lib.moe_combine(C.byref(s), L, 0x50000, q.MOE_BF16, 4, eo, 0xA0000, 0x70000, y, res, 0x80000,
+                               1 << 30, None)
+
+    def prefill(eo=0x60000, y=0x90000, res=None):
+        return lib.moe_layer_prefill(C.byref(s), L, 0x50000, q.MOE_BF16, 4, None, 0xB0000, 0x70000, 0xC0000,
+                                     0xD0000, 0xE0000, 0xA0000, eo, y, res, 0x80000, 1 << 30, None)
+
+    for call in (combine, prefill):
+        assert call(eo=0x60004) == q.MOE_ERR_INVALID_ARG
+        assert call(y=0x90008) == q.MOE_ERR_INVALID_ARG
+        assert call(res=0x50002) == q.MOE_ERR_INVALID_ARG
+
+
 def test_status_strings():
     for st in (q.MOE_OK, q.MOE_ERR_INVALID_ARG, q.MOE_ERR_UNSUPPORTED_SHAPE, q.MOE_ERR_WORKSPACE, q.MOE_ERR_HIP,
                q.MOE_ERR_DEVICE_CHECK):
