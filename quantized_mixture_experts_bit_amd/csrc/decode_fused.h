@@ -88,6 +88,7 @@ struct FusedSmem {
   float hsum[48];            // sums of h (hi + lo) per group
   float red[2][4][64];
   double rd[256];
+  double rd2[32];
   double lg[256];
   uint64_t key[256];
   uint32_t lgw[512];
@@ -358,9 +359,19 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
   }
   S.rd[tid] = acc;
   __syncthreads();
+  // the 128 partials of expert e (entries of parity e) in two levels: 16 threads per
+  // expert add 8 each, then one thread adds those 16
+  if (tid < 32) {
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a += S.rd[tid + 32 * i];
+    S.rd2[tid] = a;
+  }
+  __syncthreads();
   if (tid < kFusedRouterE) {
     double l = 0.0;
-    for (int k = 0; k < 128; ++k) l += S.rd[tid + 2 * k];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) l += S.rd2[tid + 2 * k];
     if (F.offset) l += (double)F.offset[e0 + tid];
     S.lgv[tid] = l;
   }
