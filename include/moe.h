@@ -161,6 +161,9 @@ moe_status moe_router_topk(const moe_shape* shape, const moe_layer* layer, const
  *   count [n_experts], offset [n_experts+1] (exclusive prefix sum of count),
  *   perm [rows*top_k] (pair id at each sorted position),
  *   inv_perm [rows*top_k] (sorted position of each pair). Bit-exact.
+ * An id outside [0, n_experts) is recorded as MOE_DEVERR_BAD_EXPERT_ID and its
+ * pair is left out: count/offset/perm cover the other pairs (perm entries from
+ * offset[n_experts] on are not written) and its inv_perm is -1.
  */
 moe_status moe_group_by_expert(const moe_shape* shape, const int32_t* topk_idx, int32_t rows, int32_t* count,
                                int32_t* offset, int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,

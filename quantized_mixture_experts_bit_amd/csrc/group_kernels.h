@@ -26,6 +26,7 @@ __device__ __forceinline__ uint64_t match_lanes(int e, bool valid) {
 }
 
 constexpr int kGroupWaves = 16;  // one workgroup of 1024 threads
+constexpr int kGroupRounds = 4;  // rounds of 64 pairs per wave kept in registers between the passes
 
 // Stable counting sort of the (row, slot) pairs by expert, in one workgroup.
 // Wave w owns the pairs [w*S, (w+1)*S) (S a multiple of 64) and walks them 64 at
@@ -35,7 +36,9 @@ constexpr int kGroupWaves = 16;  // one workgroup of 1024 threads
 // scanned in wave order, and the totals across experts. Pass 2 walks the pairs
 // again: a pair's position is its expert's offset + the pairs of that expert in
 // earlier waves + those in earlier rounds of its wave (the running count) + the
-// matching lanes below it. The result is the order (expert, pair) exactly.
+// matching lanes below it. The result is the order (expert, pair) exactly. The
+// first kGroupRounds rounds of a wave keep their ids and lane matches in registers
+// from pass 1 to pass 2.
 __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ topk_idx, int n_pairs, int n_experts,
                                                 int32_t* __restrict__ count, int32_t* __restrict__ offset,
                                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
@@ -43,30 +46,51 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ topk
   __shared__ int32_t off[256];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int i = t; i < kGroupWaves * n_experts; i += 1024) cnt[i] = 0;
-  __syncthreads();
   const int S = ((n_pairs + kGroupWaves - 1) / kGroupWaves + 63) & ~63;
   const int p_end = min(n_pairs, (w + 1) * S);
+  // ids of the first rounds: every load issued before the counters are cleared
+  int ids[kGroupRounds];
+#pragma unroll
+  for (int r = 0; r < kGroupRounds; ++r) {
+    const int p = w * S + 64 * r + lane;
+    ids[r] = p < p_end ? topk_idx[p] : -1;
+  }
+  for (int i = t; i < kGroupWaves * n_experts; i += 1024) cnt[i] = 0;
+  __syncthreads();
   int32_t* mine = cnt + w * n_experts;
-  for (int p0 = w * S; p0 < p_end; p0 += 64) {
-    const int p = p0 + lane;
-    int e = p < p_end ? topk_idx[p] : -1;
-    if (p < p_end && (e < 0 || e >= n_experts)) {  // not an expert id: reported, and the pair is dropped
+  // pass 1; an id that is not an expert id is reported and its pair dropped
+  auto count_round = [&](int p, int e) __attribute__((always_inline)) {
+    if (p < p_end && (e < 0 || e >= n_experts)) {
       flag_device_error(2u);
       e = -1;
     }
-    const bool valid = e >= 0;
-    const uint64_t m = match_lanes(e, valid);
-    if (valid && (m & below) == 0) mine[e] += __popcll(m);
+    const uint64_t m = match_lanes(e, e >= 0);
+    if (e >= 0 && (m & below) == 0) mine[e] += __popcll(m);
+    return m;
+  };
+  uint64_t match[kGroupRounds];
+#pragma unroll
+  for (int r = 0; r < kGroupRounds; ++r) {
+    if (w * S + 64 * r >= p_end) break;  // wave-uniform
+    const int p = w * S + 64 * r + lane;
+    match[r] = count_round(p, ids[r]);
+    if (ids[r] >= n_experts) ids[r] = -1;
+  }
+  for (int p0 = w * S + 64 * kGroupRounds; p0 < p_end; p0 += 64) {
+    const int p = p0 + lane;
+    (void)count_round(p, p < p_end ? topk_idx[p] : -1);
   }
   __syncthreads();
-  // per expert: wave counts -> starts within the expert, in wave order
+  // per expert: wave counts -> starts within the expert, in wave order (all read first)
   for (int e = t; e < n_experts; e += 1024) {
+    int c[kGroupWaves];
+#pragma unroll
+    for (int ww = 0; ww < kGroupWaves; ++ww) c[ww] = cnt[ww * n_experts + e];
     int run = 0;
+#pragma unroll
     for (int ww = 0; ww < kGroupWaves; ++ww) {
-      const int c = cnt[ww * n_experts + e];
       cnt[ww * n_experts + e] = run;
-      run += c;
+      run += c[ww];
     }
     off[e] = run;  // total for now
   }
@@ -100,22 +124,28 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ topk
     if (lane == 63) offset[n_experts] = incl;
   }
   __syncthreads();
-  for (int p0 = w * S; p0 < p_end; p0 += 64) {
-    const int p = p0 + lane;
-    int e = p < p_end ? topk_idx[p] : -1;
-    if (e >= n_experts) e = -1;
-    const bool valid = e >= 0;
-    const uint64_t m = match_lanes(e, valid);
-    if (valid) {
+  // pass 2; every lane reads the running count before the lowest lane of each group
+  // advances it (one wavefront, LDS operations in order)
+  auto place = [&](int p, int e, uint64_t m) __attribute__((always_inline)) {
+    if (e >= 0) {
       const int pos = off[e] + mine[e] + __popcll(m & below);
       perm[pos] = p;
       inv_perm[p] = pos;
     } else if (p < p_end) {
       inv_perm[p] = -1;
     }
-    // every lane has read the running count above before the lowest lane of each
-    // group advances it (one wavefront, LDS operations in order)
-    if (valid && (m & below) == 0) mine[e] += __popcll(m);
+    if (e >= 0 && (m & below) == 0) mine[e] += __popcll(m);
+  };
+#pragma unroll
+  for (int r = 0; r < kGroupRounds; ++r) {
+    if (w * S + 64 * r >= p_end) break;  // wave-uniform
+    place(w * S + 64 * r + lane, ids[r], match[r]);
+  }
+  for (int p0 = w * S + 64 * kGroupRounds; p0 < p_end; p0 += 64) {
+    const int p = p0 + lane;
+    int e = p < p_end ? topk_idx[p] : -1;
+    if (e >= n_experts) e = -1;
+    place(p, e, match_lanes(e, e >= 0));
   }
 }
 

@@ -18,7 +18,7 @@ def zipf(shape):
 
 
 @pytest.mark.parametrize("rows,E,k", [(1, 128, 8), (8, 128, 8), (128, 128, 8), (256, 128, 8), (37, 64, 1),
-                                      (200, 256, 16), (3, 64, 16)])
+                                      (200, 256, 16), (3, 64, 16), (1000, 64, 16), (4095, 128, 16)])
 def test_grouping_bit_exact(rows, E, k):
     rng = np.random.default_rng(rows * 31 + E + k)
     skew = np.exp(-np.arange(E) / 8.0)
@@ -34,6 +34,32 @@ def test_grouping_bit_exact(rows, E, k):
     np.testing.assert_array_equal(off.cpu().numpy(), ro)
     np.testing.assert_array_equal(perm.cpu().numpy(), rp)
     np.testing.assert_array_equal(inv.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("rows,E,k", [(40, 128, 8), (600, 64, 8)])
+def test_grouping_drops_invalid_ids(rows, E, k):
+    """Ids outside [0, E) are reported and their pairs left out: the valid pairs sort as
+    the oracle sorts them alone, an invalid pair's inv_perm is -1."""
+    rng = np.random.default_rng(rows + E)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(rows)]).astype(np.int32)
+    bad = rng.random(idx.shape) < 0.04
+    idx[bad] = rng.choice([-1, -100, E, E + 7], size=int(bad.sum()))
+    shape = q.MoeShape(512, 256, 512, n_experts=E, top_k=k)
+    cnt, off = empty_i32(E), empty_i32(E + 1)
+    perm, inv = empty_i32(rows * k), empty_i32(rows * k)
+    ws = torch.empty(q.moe_workspace_bytes(shape, rows), dtype=torch.uint8, device=device())
+    q.moe_group_by_expert(shape, torch.from_numpy(idx).to(device()), rows, cnt, off, perm, inv, ws)
+    assert q.moe_check_device_error() & q.MOE_DEVERR_BAD_EXPERT_ID
+    flat = idx.reshape(-1)
+    valid = np.flatnonzero(~bad.reshape(-1))
+    rc, ro, rp, ri = O.group_by_expert(flat[valid].reshape(-1, 1), E)  # the valid pairs as rows of one pick
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(off.cpu().numpy(), ro)
+    np.testing.assert_array_equal(perm.cpu().numpy()[:valid.size], valid[rp])
+    want_inv = np.full(rows * k, -1, dtype=np.int32)
+    want_inv[valid] = ri
+    np.testing.assert_array_equal(inv.cpu().numpy(), want_inv)
+    assert q.moe_check_device_error() == 0
 
 
 def run_layer_prefill(shape, dl, x, ws, offset=None, residual=None):
