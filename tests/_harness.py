@@ -29,6 +29,10 @@ def device():
 # and few experts, few picks, groups that do not fill a 4-group block
 WIDE = synth.MoeShape(1024, 256, 768, n_experts=256, top_k=16)
 NARROW = synth.MoeShape(768, 192, 320, n_experts=64, top_k=4)
+# shapes past the whole-block decode kernel's tiling (d_ff <= 768; d_model <= 3072 and
+# d_ff_shared <= 2560), which moe_layer_decode serves with its three-launch path
+BEYOND_FF = synth.MoeShape(1024, 832, 512, n_experts=64, top_k=4)
+BEYOND_D = synth.MoeShape(3200, 256, 2624, n_experts=64, top_k=2)
 
 
 def get_layer(shape, seed=0, layer=0, variant=synth.Variant()):

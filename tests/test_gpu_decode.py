@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 import synth
-from _harness import (NARROW, REL_TOL, WIDE, check_topk, empty_f32, empty_i32, get_layer, rel_err, to_dev_x,
+from _harness import (BEYOND_D, BEYOND_FF, NARROW, REL_TOL, WIDE, check_topk, empty_f32, empty_i32, get_layer, rel_err, to_dev_x,
                       workspace, device)
 
 pytestmark = pytest.mark.gpu
@@ -22,6 +22,8 @@ CASES = [
     pytest.param(synth.GEMMA4, "bf16", SOFT, id="gemma4-bf16-soft"),
     pytest.param(WIDE, "bf16", SOFT, id="wide256x16-bf16-soft"),
     pytest.param(NARROW, "f32", SOFT, id="narrow64x4-f32-soft"),
+    pytest.param(BEYOND_FF, "f32", SOFT, id="three-launch-dff832-f32-soft"),
+    pytest.param(BEYOND_D, "bf16", SOFT, id="three-launch-d3200-bf16-soft"),
 ]
 
 

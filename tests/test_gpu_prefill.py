@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 import synth
-from _harness import (NARROW, REL_TOL, WIDE, check_topk, device, empty_f32, empty_i32, get_layer, rel_err,
+from _harness import (BEYOND_FF, NARROW, REL_TOL, WIDE, check_topk, device, empty_f32, empty_i32, get_layer, rel_err,
                       to_dev_x, workspace)
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +84,7 @@ PREFILL_CASES = [
     pytest.param(synth.GEMMA4, 64, "f32", None, "zipf", id="gemma4-64rows-f32-zipf"),
     pytest.param(WIDE, 40, "bf16", synth.Variant(router_scale_log2=-6), None, id="wide256x16-40rows-soft"),
     pytest.param(NARROW, 33, "f32", synth.Variant(router_scale_log2=-6), None, id="narrow64x4-33rows-f32-soft"),
+    pytest.param(BEYOND_FF, 21, "f32", synth.Variant(router_scale_log2=-6), None, id="dff832-21rows-f32-soft"),
     # the most rows a call takes (rows * top_k < 65536): every expert gets many 64-row tiles
     pytest.param(synth.GEMMA4, 65535 // 8, "bf16", None, None, id="gemma4-8191rows-max"),
 ]
