@@ -18,10 +18,16 @@
 // (0x4300 | q is the bf16 value 128 + q for q < 16).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qmoe {
+
+// a compile-time int as a value (selects template code from a runtime branch)
+template <int I>
+using ic = std::integral_constant<int, I>;
 
 constexpr int kGroup = 64;
 constexpr int kTile4 = 2304;

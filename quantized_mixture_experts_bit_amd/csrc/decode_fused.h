@@ -92,7 +92,7 @@ struct FusedSmem {
   double lg[256];
   uint64_t key[256];
   uint32_t lgw[512];
-  uint32_t kp[256];
+  __attribute__((aligned(16))) uint32_t kp[256];
   int rank[4][256];
   uint32_t slots[256];
   float eo[17][64];
@@ -271,23 +271,28 @@ __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, Fu
     S.kp[tid] = ((uint32_t)(key >> (33 + idbits)) << idbits) | (uint32_t)(E - 1 - tid);
   }
   __syncthreads();
-  // thread t: expert t % E against the competitors of share t / E (256 / E shares)
-  const int parts = E == 64 ? 4 : E == 128 ? 2 : 1;
-  const int per = E / parts, h = tid / E, me = tid % E;
+  // thread t: expert t % E against the competitors of share t / E (256 / E shares of
+  // 64, 64 or 16 keys, all of a 32-key run read before the first comparison)
+  const int lgE = E == 64 ? 6 : E == 128 ? 7 : 8;
+  const int parts = 256 >> lgE, h = tid >> lgE, me = tid & (E - 1);
   const int mine = (int)S.kp[me];
   int r4[4] = {0, 0, 0, 0};
-  if (h < parts) {
-    for (int c0 = h * per; c0 < (h + 1) * per; c0 += 16) {
-      u32x4_t kk[4];
+  auto count = [&](auto nc, int c0) __attribute__((always_inline)) {
+    constexpr int N = decltype(nc)::value;
+    u32x4_t kk[N / 4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kk[i] = *reinterpret_cast<const u32x4_t*>(&S.kp[c0 + 4 * i]);
+    for (int i = 0; i < N / 4; ++i) kk[i] = *reinterpret_cast<const u32x4_t*>(&S.kp[c0 + 4 * i]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < N / 4; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) r4[c] += (int)((uint32_t)(mine - (int)kk[i][c]) >> 31);
-    }
-    S.rank[h][me] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+      for (int c = 0; c < 4; ++c) r4[c] += (int)((uint32_t)(mine - (int)kk[i][c]) >> 31);
+  };
+  if (parts == 4) {
+    count(ic<16>{}, 16 * h);
+  } else {
+    for (int c0 = h * (E / parts); c0 < (h + 1) * (E / parts); c0 += 32) count(ic<32>{}, c0);
   }
+  S.rank[h][me] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
   __syncthreads();
   if (tid < E) {
     int rk = 0;

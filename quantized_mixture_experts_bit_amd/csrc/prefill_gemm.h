@@ -51,8 +51,6 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
-template <int I>
-using ic = std::integral_constant<int, I>;
 
 struct PrefillArgs {
   const uint8_t* pool;
