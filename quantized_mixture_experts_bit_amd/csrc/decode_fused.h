@@ -96,8 +96,6 @@ struct FusedSmem {
   int rank[4][256];
   uint32_t slots[256];
   float eo[17][64];
-  float gu[2][kFusedRows];
-  float hv[kFusedRows];
   double lgv[kFusedRouterE];
   int sel_e[17];
   float selw[16];
@@ -482,22 +480,19 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
   S.red[0][wave][lane] = acc[0];
   S.red[1][wave][lane] = acc[1];
   __syncthreads();
-  if (tid < 2 * kFusedRows) {
-    const int mat = tid >> 4, r = tid & 15;
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) v += S.red[mat][w][r + 16 * k4];
-    S.gu[mat][r] = v;
-  }
-  __syncthreads();
-  if (tid < kFusedRows) S.hv[tid] = gelu_tanh(S.gu[0][tid]) * S.gu[1][tid];
-  __syncthreads();
+  // the thread that stores copy c of row r adds that row's gate and up partials itself
+  // (the same order in every copy), so no further barrier stands before the stores
   if (tid < kFusedRows * kHCopies) {
     const int r = tid % kFusedRows, copy = tid / kFusedRows;
+    float v[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) v[mat] += S.red[mat][w][r + 16 * k4];
     put_tag(&F.h_tag[copy * F.h_stride + (size_t)slot * F.fmax + nb * 64 + q4 * kFusedRows + r],
-            __float_as_uint(S.hv[r]), tag);
+            __float_as_uint(gelu_tanh(v[0]) * v[1]), tag);
   }
 }
 
