@@ -532,6 +532,7 @@ __global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first,
 struct DownSmem {
   __attribute__((aligned(16))) uint16_t Hl[2][64 * kLdsStride];
   float rowinv[64];
+  __attribute__((aligned(16))) float agL[2][64];  // per-row sums of the staged H group
 };
 
 // One work item = (64-row tile, two blocks of 64 output columns, 2 np and 2 np + 1).
@@ -577,11 +578,24 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     ha[slot][0] = bld16(hres, hvo, so);
     ha[slot][1] = bld16(hres, hvo + 16, so);
   };
+  // the staging threads also add up each row's group (dot products against fp16 (1, 1)
+  // pairs, the four threads of a row summed by DPP) for the bias term of the epilogue
   auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(&Hl[buf][hr * kLdsStride + hq * 16]);
     dst[0] = ha[slot][0];
     dst[1] = ha[slot][1];
+    float v = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w = ha[slot][h][c];  // a bit_cast of the vector element itself reads element 0
+        v = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3C003C00u), v, false);
+      }
+    v = dpp_add<0xB1, 0xf>(v);  // the four threads of a row are one quad
+    v = dpp_add<0x4E, 0xf>(v);
+    if (hq == 0) S.agL[buf][hr] = v;
   };
   // prologue: the loads in the order the steady state issues them (weights of group
   // j, then activations of group j + 1), so the wait counts agree on entry
@@ -602,7 +616,6 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int m = 0; m < kDownBlocks; ++m) zero_acc(acc[mb][m]);
-  const f16x8_t ones = __builtin_bit_cast(f16x8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
   // one K group, as in the gate/up kernel
   const NibKT<0x64006400u> nk;
@@ -625,7 +638,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
         const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
         const f16x8_t a0 = lds_frag<f16x8_t>(&Hl[buf][ao]);
         const f16x8_t a1 = lds_frag<f16x8_t>(&Hl[buf][ao + 32]);
-        const f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        const f32x4_t ag = *reinterpret_cast<const f32x4_t*>(&S.agL[buf][16 * mb + 4 * (lane >> 4)]);
 #pragma unroll
         for (int m = 0; m < kDownBlocks; ++m) {
           const f32x4_t t = mfma(a1, b1[m], mfma(a0, b0[m], f32x4_t{0.f, 0.f, 0.f, 0.f}));
