@@ -62,6 +62,15 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int t) {
   return ((w >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
 }
 
+// power of two that brings a row maximum m (> 0) into [2^14, 2^15); 1 for m == 0
+__device__ __forceinline__ float row_scale(float m) {
+  if (!(m > 0.0f)) return 1.0f;
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;  // floor(log2 m) for normal m
+  return ldexpf(1.0f, min(14 - e, 126));
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
 // nib_pair with its two constants held in registers (the mask in an SGPR, the exponent
 // bits in a VGPR): a pair is then one shift and one v_and_or_b32, where literal
 // operands cost a shift, an and and an or.

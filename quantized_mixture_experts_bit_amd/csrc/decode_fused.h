@@ -85,7 +85,8 @@ struct FusedArgs {
 struct FusedSmem {
   __attribute__((aligned(16))) uint32_t xb[kFusedXWords];  // x pairs (or values), or h hi | lo pairs
   float xg[2 * kFusedMaxG];  // sums of x over 32-column halves of each group
-  float hsum[48];            // sums of h (hi + lo) per group
+  float hsum[48];            // sums of the scaled fp16 h per group
+  float hmax[4];
   float red[2][4][64];
   double rd[256];
   double rd2[32];
@@ -498,37 +499,34 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
 
 // ------------------------------------------------------------------ down item (+ combine)
 
-// group sum of one row against h in LDS as 32 hi and 32 lo pairs (hh, hl point at the
-// group's pair 0), read in two batches of 16 pairs (one LDS wait each)
-__device__ __forceinline__ float group_dot_lds(const uint32_t* hh, const uint32_t* hl, uint4 qa, uint4 qb,
-                                               uint32_t sbw, float Vg) {
+// group sum of one row against h in LDS as 32 fp16 pairs (hh points at the group's
+// pair 0; h scaled by the item's power of two), read in two batches of 16 pairs (one
+// LDS wait each). The codes enter as fp16 pairs (1024 + q, 1024 + q'), one shift and
+// one v_and_or_b32 each, and 1024 goes into the bias: s * sum (1024 + q) h + (b - 1024 s) V.
+__device__ __forceinline__ float group_dot_lds(const uint32_t* hh, uint4 qa, uint4 qb, uint32_t sbw, float Vg) {
   const uint32_t words[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
   float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const NibK nk;
+  const NibKT<0x64006400u> nk;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    uint4 h4[4], l4[4];
+    uint4 h4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h4[i] = *reinterpret_cast<const uint4*>(hh + 16 * half + 4 * i);
-      l4[i] = *reinterpret_cast<const uint4*>(hl + 16 * half + 4 * i);
-    }
+    for (int i = 0; i < 4; ++i) h4[i] = *reinterpret_cast<const uint4*>(hh + 16 * half + 4 * i);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const uint32_t w = words[4 * half + jj];
       const uint32_t hv[4] = {h4[jj].x, h4[jj].y, h4[jj].z, h4[jj].w};
-      const uint32_t lv[4] = {l4[jj].x, l4[jj].y, l4[jj].z, l4[jj].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t p = nk.pair(w, t);
-        acc4[t] = dot2(p, hv[t], acc4[t]);
-        acc4[t] = dot2(p, lv[t], acc4[t]);
+        acc4[t] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p), __builtin_bit_cast(f16x2_t, hv[t]), acc4[t],
+                                         false);
       }
     }
   }
   const float a = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   const float s = bf16_lo(sbw), b = bf16_hi(sbw);
-  return fmaf(s, a, fmaf(-128.0f, s, b) * Vg);
+  return fmaf(s, a, fmaf(-1024.0f, s, b) * Vg);
 }
 
 // weights of one 64-row block for groups g0 + wave + 4i (i < GW) of [g0, g1), loaded ahead of use
@@ -548,49 +546,67 @@ struct RowLoads {
       }
     }
   }
-  // against h in LDS: pairs of group g at hh/hl + g * 32, group sums at gs[g]
-  __device__ __forceinline__ float dot_lds(int g0, int g1, int wave, const uint32_t* hh, const uint32_t* hl,
-                                           const float* gs) const {
+  // against h in LDS: fp16 pairs of group g at hh + g * 32, group sums at gs[g]
+  __device__ __forceinline__ float dot_lds(int g0, int g1, int wave, const uint32_t* hh, const float* gs) const {
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
       const int g = g0 + wave + 4 * i;
-      if (g < g1) acc += group_dot_lds(hh + g * 32, hl + g * 32, qa[i], qb[i], sb[i], gs[g]);
+      if (g < g1) acc += group_dot_lds(hh + g * 32, qa[i], qb[i], sb[i], gs[g]);
     }
     return acc;
   }
 };
 
-// Values [j0, j1) of one slot's h (j0, j1 multiples of 64) from their tagged words into
-// LDS at the same positions, as hi and lo bf16 halves (hi pairs at xb, lo pairs at
-// xb + kFusedXWords/2), with the per-group sums of hi + lo.
+// Values [j0, j1) of one slot's h (j0, j1 multiples of 64, j1 - j0 <= 256 kGatherPer)
+// from their tagged words into LDS at the same positions as fp16 of h * sc, with sc the
+// power of two that brings their largest |h| into [2^14, 2^15) (the prefill's H
+// scaling), and the per-group sums of those fp16 values in S.hsum. Returns sc.
 // on_first_in() (kWatch) runs once, as soon as the first values are in.
+constexpr int kGatherPer = 5;
 template <bool kWatch = false, typename Hook = void (*)()>
-__device__ __forceinline__ void gather_h(const uint64_t* src, int j0, int j1, uint32_t tag, FusedSmem& S,
-                                         Hook on_first_in = nullptr) {
-  uint16_t* hh = reinterpret_cast<uint16_t*>(S.xb);
-  uint16_t* hl = reinterpret_cast<uint16_t*>(S.xb + kFusedXWords / 2);
+__device__ __forceinline__ float gather_h(const uint64_t* src, int j0, int j1, uint32_t tag, FusedSmem& S,
+                                          Hook on_first_in = nullptr) {
+  float* hf = reinterpret_cast<float*>(S.xb);
   for (int base = j0; base < j1; base += 1024)
     poll_tagged<4, kWatch>(
         [&](int i) { return src + base + i; }, min(1024, j1 - base), tag,
-        [&](int i, uint32_t p) {
-          const float h = __uint_as_float(p);
-          const uint32_t hi = f32_to_bf16_bits(h);
-          hh[base + i] = (uint16_t)hi;
-          hl[base + i] = (uint16_t)f32_to_bf16_bits(h - bf16_to_f32((uint16_t)hi));
-        },
-        [](int) { return false; }, [] {},
+        [&](int i, uint32_t p) { hf[base + i] = __uint_as_float(p); }, [](int) { return false; }, [] {},
         [&] {
           if constexpr (kWatch) on_first_in();
         });
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int gi = j0 / kGroup + wave; gi < j1 / kGroup; gi += 4) {
-    const int i = gi * kGroup + lane;
-    const float s = wave_sum(bf16_to_f32(hh[i]) + bf16_to_f32(hl[i]));
-    if (lane == 0) S.hsum[gi] = s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // thread t holds values j0 + t + 256 k: wave w, value k is group j0/64 + 4 k + w
+  float v[kGatherPer];
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kGatherPer; ++k) {
+    const int j = j0 + tid + 256 * k;
+    v[k] = j < j1 ? hf[j] : 0.0f;
+    m = fmaxf(m, fabsf(v[k]));  // a NaN is skipped, as fmaxf does
+  }
+  m = row16_max(m);
+  m = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0)),
+                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16))),
+            fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32)),
+                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48))));
+  if (lane == 0) S.hmax[wave] = m;
+  __syncthreads();  // also: every fp32 value is read before the fp16 writes below
+  const float sc = row_scale(fmaxf(fmaxf(S.hmax[0], S.hmax[1]), fmaxf(S.hmax[2], S.hmax[3])));
+  uint16_t* hh = reinterpret_cast<uint16_t*>(S.xb);
+#pragma unroll
+  for (int k = 0; k < kGatherPer; ++k) {
+    const int j = j0 + tid + 256 * k;
+    if (j0 + 256 * k + 64 * wave < j1) {  // wave-uniform: j1 - j0 is a multiple of 64
+      const _Float16 hv = (_Float16)(v[k] * sc);
+      hh[j] = __builtin_bit_cast(uint16_t, hv);
+      const float gsum = wave_sum((float)hv);
+      if (lane == 0) S.hsum[j / kGroup] = gsum;
+    }
   }
   __syncthreads();
+  return sc;
 }
 
 // The picks and their softmax weights into S.sel_e, S.selw (fp64 softmax over the
@@ -651,22 +667,23 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
   RowLoads<GW> w;
   const uint8_t* rowblock = blob ? blob + 2 * m4_bytes(Fd, F.d) + (uint64_t)ob * Gin * kTile4 : nullptr;
   const uint64_t* hsrc = F.h_tag + (blockIdx.x % kHCopies) * F.h_stride + (size_t)slot * F.fmax;
+  float sc = 1.0f;
   if (kind == 0) {
     // a routed expert's down weights wait until its h starts to come in, so that they do
     // not take memory bandwidth from the gate/up loads h depends on; they arrive while
     // the rest of h is produced
     if (tid == 0) arrive_epoch(F, epoch);
-    gather_h<true>(hsrc, g0 * kGroup, g1 * kGroup, tag, S, [&] {
+    sc = gather_h<true>(hsrc, g0 * kGroup, g1 * kGroup, tag, S, [&] {
       if (rowblock) w.load(rowblock, g0, g1, wave, lane);
     });
   } else {
     if (rowblock) w.load(rowblock, g0, g1, wave, lane);
     if (tid == 0) arrive_epoch(F, epoch);
     if (kind == 2) pick_weights(F, tag, S);  // the logits are out long before the shared h
-    gather_h(hsrc, g0 * kGroup, g1 * kGroup, tag, S);
+    sc = gather_h(hsrc, g0 * kGroup, g1 * kGroup, tag, S);
   }
-  const float acc = rowblock ? w.dot_lds(g0, g1, wave, S.xb, S.xb + kFusedXWords / 2, S.hsum) : 0.0f;
-  const float r = reduce_waves4(acc, S.red[0], wave, lane);
+  const float acc = rowblock ? w.dot_lds(g0, g1, wave, S.xb, S.hsum) : 0.0f;
+  const float r = reduce_waves4(acc, S.red[0], wave, lane) * (1.0f / sc);  // exact: sc is a power of two
   if (kind == 2) {
     fused_combine(F, ob, r, tag, S);
   } else if (wave == 0) {

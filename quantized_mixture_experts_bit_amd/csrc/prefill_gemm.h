@@ -170,14 +170,6 @@ __device__ __forceinline__ void xcd_item(int b, int nt, int nc, int& mt, int& c)
   c = r / k;
 }
 
-// power of two that brings a row maximum m (> 0) into [2^14, 2^15); 1 for m == 0
-__device__ __forceinline__ float row_scale(float m) {
-  if (!(m > 0.0f)) return 1.0f;
-  const int e = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;  // floor(log2 m) for normal m
-  return ldexpf(1.0f, min(14 - e, 126));
-}
-
-__device__ __forceinline__ uint16_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 // B operand, gate/up: the 8 codes of one packed word as bf16 (128 + q)
 __device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w, const NibK& nk) {
