@@ -54,7 +54,7 @@ constexpr int kSyncLine = 32;        // words per 128-byte line: one sync word p
 constexpr int kEpochCopies = 64;     // epoch copy c at line c
 constexpr int kArrivalCounters = 32; // arrival counter i at line kEpochCopies + i
 constexpr int kFusedSyncWords = (kEpochCopies + kArrivalCounters) * kSyncLine;
-constexpr int kFusedXWords = 3072;   // LDS words holding x (or h as hi and lo bf16 halves)
+constexpr int kFusedXWords = 3072;   // LDS words holding x, or h (fp32, then scaled fp16)
 constexpr int kFusedMaxG = 48;       // d_model / 64
 constexpr int kFusedGuI = 6;         // gate/up loads per lane and matrix: group pairs / 4 waves
 constexpr int kFusedRoutedGW = 3;    // routed down: groups of d_ff per wave (d_ff <= 768)
@@ -83,7 +83,7 @@ struct FusedArgs {
 };
 
 struct FusedSmem {
-  __attribute__((aligned(16))) uint32_t xb[kFusedXWords];  // x pairs (or values), or h hi | lo pairs
+  __attribute__((aligned(16))) uint32_t xb[kFusedXWords];  // x pairs (or values), or h
   float xg[2 * kFusedMaxG];  // sums of x over 32-column halves of each group
   float hsum[48];            // sums of the scaled fp16 h per group
   float hmax[4];
