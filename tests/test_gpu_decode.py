@@ -106,6 +106,32 @@ def test_layer_decode(shape, dt, variant):
     assert q.moe_check_device_error() == 0
 
 
+@pytest.mark.parametrize("log2_scale,dt", [(6, "f32"), (6, "bf16"), (-10, "f32")],
+                         ids=["x-times-64-f32", "x-times-64-bf16", "x-over-1024-f32"])
+def test_layer_decode_far_from_unit_scale(log2_scale, dt):
+    """Activations scaled by a power of two: with x * 64 the GeGLU output h passes the
+    fp16 range, with x / 1024 it sits far below 1; the down GEMV scales h by a power of
+    two of its own, so y still meets the tolerance against the oracle."""
+    shape = synth.GEMMA4
+    L, ol, dl = get_layer(shape)
+    ws = workspace(shape, 1)
+    xf = synth.make_x(shape, 1, seed=9, dtype="f32") * np.float32(2.0 ** log2_scale)
+    x = xf if dt == "f32" else synth.f32_to_bf16_bits(xf)
+    ref = O.moe_rows(ol, x)
+    # the premise, from the oracle: the first pick's h = gelu(gate x) * (up x)
+    e0 = L.experts[int(ref["idx"][0, 0])]
+    xr = O.x_to_f64(x)[0]
+    h = np.array([O.gelu_tanh(g) for g in O.matvec(e0.gate, xr)]) * O.matvec(e0.up, xr)
+    assert (np.abs(h).max() > 65504.0) if log2_scale > 0 else (np.abs(h).max() < 1.0)
+    idx, w, eo, y = run_layer_decode(shape, dl, x, ws)
+    if check_topk(idx, ref, shape.top_k)[0]:
+        ref = O.moe_rows(ol, x, idx=idx.reshape(1, -1))
+    assert rel_err(y, ref["y"][0]) <= REL_TOL
+    for j in range(shape.top_k):
+        assert rel_err(eo[j], ref["expert_out"][0, j]) <= REL_TOL
+    assert q.moe_check_device_error() == 0
+
+
 def test_layer_decode_onehot_is_one_dense_ffn():
     shape = synth.TINY
     L, ol, dl = get_layer(shape, variant=synth.Variant(shared_zero=True))
