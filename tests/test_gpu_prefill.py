@@ -126,6 +126,27 @@ def test_layer_prefill(shape, rows, dt, variant, skew):
         assert (got["cnt"] > 0).sum() < 60 and got["cnt"].max() >= rows // 2
 
 
+@pytest.mark.parametrize("log2_scale", [6, -10], ids=["x-times-64", "x-over-1024"])
+def test_layer_prefill_far_from_unit_scale(log2_scale):
+    """Rows scaled by powers of two (H past the fp16 range, or far below 1), each row by
+    a different power within a factor of 8 of the next: the per-row H scale keeps every
+    row within the tolerance of the oracle."""
+    shape = synth.GEMMA4
+    L, ol, dl = get_layer(shape)
+    rows = 24
+    row_scale = np.float32(2.0) ** (log2_scale + np.arange(rows) % 4 - 2).astype(np.float32)
+    x = synth.make_x(shape, rows, seed=13, dtype="f32") * row_scale[:, None]
+    ws = workspace(shape, rows)
+    got = run_layer_prefill(shape, dl, x, ws)
+    sel = np.arange(0, rows, 3)
+    ref = O.moe_rows(ol, x[sel])
+    if check_topk(got["idx"][sel], ref, shape.top_k).any():
+        ref = O.moe_rows(ol, x[sel], idx=got["idx"][sel])
+    for i, r in enumerate(sel):
+        assert rel_err(got["y"][r], ref["y"][i]) <= REL_TOL, "row %d" % r
+    assert q.moe_check_device_error() == 0
+
+
 def test_prefill_chunk_split_calls_match_fused():
     shape = synth.GEMMA4
     L, ol, dl = get_layer(shape)
