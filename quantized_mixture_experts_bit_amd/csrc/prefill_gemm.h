@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_gateup(PrefillArgs A, const 
 // by the shared rows): the row's power-of-two scale from its per-block maxima, then
 // the fp16 copy of h * scale. Every load of a round (the maxima and up to
 // kHconvLoads 16-byte pieces of the row per lane) is issued before any is used.
-constexpr int kHconvLoads = 8;
+constexpr int kHconvLoads = 9;
 __global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first, int count) {
   const int lane = threadIdx.x & 63;
   const int r = first + (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
