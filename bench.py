@@ -464,6 +464,58 @@ def main():
                 % (name, rec["ms_per_token"], rec["tokens_per_s"], rec["hit_rate"], rec["misses_per_token_layer"],
                    rec["bytes_per_token"] / 1e6, rec["host_to_hbm_GBps"], rec["resident_ms_per_token"],
                    rec["slowdown_vs_resident"]))
+        # prefill chunks of 128 rows through the same cache: the routed experts in passes of
+        # at most `slots` experts (MOE_SLOT_SKIP for the others), against the same split
+        # calls on the resident pool
+        RPc = 128
+        wsp = torch.empty(q.moe_workspace_bytes(shape, RPc), dtype=torch.uint8, device=dev)
+        q.moe_workspace_init(wsp)
+        po = dict(idx=torch.empty(RPc, k, dtype=torch.int32, device=dev), w=torch.empty(RPc, k, device=dev),
+                  cnt=torch.empty(E, dtype=torch.int32, device=dev), off=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                  perm=torch.empty(RPc * k, dtype=torch.int32, device=dev),
+                  inv=torch.empty(RPc * k, dtype=torch.int32, device=dev),
+                  eo=torch.empty(RPc * k, d, device=dev), y=torch.empty(RPc, d, device=dev))
+        xp_c = [torch.from_numpy(synth.make_x(shape, RPc, seed=700 + l, dtype="bf16")).view(torch.bfloat16).to(dev)
+                for l in range(NLc)]
+
+        def chunk_pass(l, through_cache):
+            if through_cache:
+                return cl[l].prefill(xp_c[l], RPc, zoff[l], po["idx"], po["w"], po["cnt"], po["off"], po["perm"],
+                                     po["inv"], po["eo"], po["y"], None, wsp)
+            q.moe_router_topk(shape, dls[l].c, xp_c[l], RPc, zoff[l], po["idx"], po["w"], None, wsp)
+            q.moe_group_by_expert(shape, po["idx"], RPc, po["cnt"], po["off"], po["perm"], po["inv"], wsp)
+            q.moe_expert_ffn_prefill_chunk(shape, dls[l].c, xp_c[l], RPc, po["off"], po["perm"], po["eo"], wsp)
+            q.moe_combine(shape, dls[l].c, xp_c[l], RPc, po["eo"], po["inv"], po["w"], po["y"], None, wsp)
+            return 0, 0
+
+        def timed_prefill(through_cache, reps):
+            for l in range(NLc):
+                chunk_pass(l, through_cache)
+            torch.cuda.synchronize()
+            h0, m0, b0 = store.stats()
+            n_pass = 0
+            t0 = time.time()
+            for _ in range(reps):
+                for l in range(NLc):
+                    n_pass += chunk_pass(l, through_cache)[0]
+            torch.cuda.synchronize()
+            dt = (time.time() - t0) / (reps * NLc)
+            h1, m1, b1 = store.stats()
+            return dt, n_pass / (reps * NLc), h1 - h0, m1 - m0, b1 - b0
+
+        reps = max(1, n_tok // 10)
+        dt_c, n_pass, hits, misses, nb = timed_prefill(True, reps)
+        dt_r = timed_prefill(False, reps)[0]
+        rec = {"workload": "prefill chunks of %d rows, Zipf(1.1)-skewed router, rotating over the %d layers" % (RPc, NLc),
+               "ms_per_chunk": dt_c * 1e3, "tokens_per_s": RPc / dt_c, "passes_per_chunk": n_pass,
+               "hit_rate": hits / max(1, hits + misses), "bytes_per_chunk": nb / (reps * NLc),
+               "host_to_hbm_GBps": nb / (reps * NLc) / dt_c / 1e9, "resident_ms_per_chunk": dt_r * 1e3,
+               "slowdown_vs_resident": dt_c / dt_r, "chunks": reps * NLc}
+        cache["prefill_zipf_router"] = rec
+        log("tiered prefill (%d rows, zipf): %.2f ms/chunk, %.2f passes/chunk, hit rate %.3f, %.1f MB/chunk from the "
+            "host tier (%.1f GB/s), resident split path %.3f ms/chunk (%.1fx)"
+            % (RPc, rec["ms_per_chunk"], rec["passes_per_chunk"], rec["hit_rate"], rec["bytes_per_chunk"] / 1e6,
+               rec["host_to_hbm_GBps"], rec["resident_ms_per_chunk"], rec["slowdown_vs_resident"]))
         store.close()
 
     # ---------------------------------------------------------------- CPU baseline (the oracle)

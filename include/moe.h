@@ -66,6 +66,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 #define MOE_DEVERR_BAD_EXPERT_ID 2u /* an expert id outside [0, n_experts) (e.g. NaN logits) */
 #define MOE_DEVERR_SYNC_TIMEOUT 4u  /* a fused-decode wait gave up; re-initialise the workspace */
 
+/* Slot-table entry that leaves an expert out of a prefill call on purpose (see
+ * moe_expert_ffn_prefill_chunk): no flag, its outputs are not written. */
+#define MOE_SLOT_SKIP 0xFFFFFFFFu
+
 /* Shape of one MoE layer. d_model, d_ff, d_ff_shared: multiples of 64;
  * n_experts: multiple of 64, at most 256; 1 <= top_k <= min(n_experts, 16);
  * group must be 64. Gemma-4-26B-A4B-like: {2816, 704, 2112, 128, 8, 64}. */
@@ -184,7 +188,12 @@ moe_status moe_expert_ffn_decode(const moe_shape* shape, const moe_layer* layer,
  * id p = perm[j], row r = p / top_k, expert e = the expert whose range holds j,
  *   expert_out[j][:] = E_e(x[r]) (unweighted), fp32 [rows*top_k][d_model].
  * Every expert's weights are read once per 64-row tile of its rows and run
- * through MFMA on bf16-dequantized tiles.
+ * through MFMA on bf16-dequantized tiles. An expert whose slot-table entry is
+ * MOE_SLOT_SKIP is left out without a flag: the rows of its pairs in expert_out
+ * keep their contents. Prefill through an expert cache smaller than a chunk's
+ * experts runs this call once per group of resident experts, each pass with a
+ * table that names that group and skips the rest (the passes write disjoint rows);
+ * the router, the grouping and moe_combine run once.
  */
 moe_status moe_expert_ffn_prefill_chunk(const moe_shape* shape, const moe_layer* layer, const void* x,
                                         moe_dtype x_dtype, int32_t rows, const int32_t* offset,

@@ -32,6 +32,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_DEVERR_BAD_SLOT = 1
 MOE_DEVERR_BAD_EXPERT_ID = 2
 MOE_DEVERR_SYNC_TIMEOUT = 4
+MOE_SLOT_SKIP = 0xFFFFFFFF
 
 
 class MoeError(RuntimeError):

@@ -210,14 +210,18 @@ __device__ uint32_t g_moe_device_error = 0;
 __device__ __forceinline__ void flag_device_error(uint32_t bits) { atomicOr(&g_moe_device_error, bits); }
 
 // blob of routed expert `e` through the slot table; nullptr (and the error flag) if the id or
-// the table entry is out of range
+// the table entry is out of range. With skip_ok, an entry MOE_SLOT_SKIP gives nullptr
+// without the flag (an expert left out of a prefill pass on purpose).
+constexpr uint32_t kSlotSkip = 0xFFFFFFFFu;
 __device__ __forceinline__ const uint8_t* expert_blob(const uint8_t* pool, uint64_t stride, uint64_t n_blobs,
-                                                      const uint32_t* slot_table, int e, int n_experts) {
+                                                      const uint32_t* slot_table, int e, int n_experts,
+                                                      bool skip_ok = false) {
   if (e < 0 || e >= n_experts) {
     flag_device_error(2u);
     return nullptr;
   }
   uint32_t b = slot_table[e];
+  if (skip_ok && b == kSlotSkip) return nullptr;
   if ((uint64_t)b >= n_blobs) {
     flag_device_error(1u);
     return nullptr;

@@ -39,6 +39,8 @@ bool shape_ok(const moe_shape* s) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+static_assert(kSlotSkip == MOE_SLOT_SKIP, "the kernels' skip entry is the one moe.h names");
+
 
 struct DecodeCfg {
   int P, Ps, fmax, nbmax;

@@ -141,7 +141,7 @@ __device__ __forceinline__ bool tile_at(const PrefillArgs& A, const TileMap& M, 
   T.m0 = __builtin_amdgcn_readfirstlane(__shfl(m0, owner, 64));
   T.mrows = __builtin_amdgcn_readfirstlane(__shfl(mr, owner, 64));
   T.F = A.f;
-  T.blob = uniform_ptr(expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, T.e, A.n_experts));
+  T.blob = uniform_ptr(expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, T.e, A.n_experts, true));
   return T.blob != nullptr;
 }
 

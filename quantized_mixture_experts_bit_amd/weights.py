@@ -19,9 +19,10 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (as_shape, moe_cache_acquire, moe_cache_create, moe_cache_destroy, moe_cache_stats,
-               moe_expert_blob_bytes, moe_layer, moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4,
-               moe_pack_matrix8, moe_router_blob_bytes, moe_shared_blob_bytes)
+from . import (MOE_SLOT_SKIP, as_shape, moe_cache_acquire, moe_cache_create, moe_cache_destroy, moe_cache_stats,
+               moe_combine, moe_expert_blob_bytes, moe_expert_ffn_prefill_chunk, moe_group_by_expert, moe_layer,
+               moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4, moe_pack_matrix8, moe_router_blob_bytes,
+               moe_router_topk, moe_shared_blob_bytes)
 
 BLOB_ALIGN = 4096  # blob stride granularity (a page)
 
@@ -147,10 +148,38 @@ class CachedLayer:
         self.c = moe_layer(store.dev_slots.data_ptr() + l * S * st, st, S,
                            store.tables.data_ptr() + l * store.shape.n_experts * 4, router.data_ptr(),
                            shared.data_ptr())
+        # the slots seen through a table of the prefill pass in flight (prefill())
+        self.pass_table = torch.empty(store.shape.n_experts, dtype=torch.int32, device=store.tables.device)
+        self.pass_view = moe_layer(store.dev_slots.data_ptr() + l * S * st, st, S, self.pass_table.data_ptr(),
+                                   router.data_ptr(), shared.data_ptr())
 
     def acquire(self, idx, slots=None, stream=None) -> int:
         """Makes the experts idx (host int32 array) resident; returns the misses."""
         return moe_cache_acquire(self.store.handle, self.l, idx, slots, stream)
+
+    def prefill(self, x, rows: int, logit_offset, topk_idx, topk_w, count, offset, perm, inv_perm, expert_out,
+                y, residual, ws):
+        """A prefill chunk through the cache: router, grouping, then the routed experts
+        in passes of at most `slots` experts (each pass makes its group resident and runs
+        the routed GEMMs with a table that names that group and skips every other expert),
+        then the shared expert and the combine. The same calls and outputs as the split
+        prefill on an all-resident pool. Returns (passes, misses)."""
+        shape, S, E = self.store.shape, self.store.slots, self.store.shape.n_experts
+        moe_router_topk(shape, self.c, x, rows, logit_offset, topk_idx, topk_w, None, ws)
+        moe_group_by_expert(shape, topk_idx, rows, count, offset, perm, inv_perm, ws)
+        need = np.flatnonzero(count.cpu().numpy() > 0).astype(np.int32)  # the host plans the passes
+        passes = misses = 0
+        for i in range(0, need.size, S):
+            group = need[i:i + S]
+            slots = np.empty(group.size, dtype=np.int32)
+            misses += self.acquire(group, slots)
+            table = np.full(E, MOE_SLOT_SKIP, dtype=np.uint32)
+            table[group] = slots
+            self.pass_table.copy_(torch.from_numpy(table.view(np.int32)))  # ordered after the previous pass
+            moe_expert_ffn_prefill_chunk(shape, self.pass_view, x, rows, offset, perm, expert_out, ws)
+            passes += 1
+        moe_combine(shape, self.c, x, rows, expert_out, inv_perm, topk_w, y, residual, ws)
+        return passes, misses
 
 
 class TieredStore:

@@ -66,3 +66,51 @@ def test_cached_decode_matches_resident(shape, slots, zipf):
             assert misses > n_layers * slots  # evictions happened
     finally:
         store.close()
+
+
+def split_prefill(shape, dl_c, x, rows, off, ws):
+    """Router, grouping, routed experts, shared + combine on the resident pool."""
+    k, d, E = shape.top_k, shape.d_model, shape.n_experts
+    o = dict(idx=empty_i32(rows, k), w=empty_f32(rows, k), cnt=empty_i32(E), off=empty_i32(E + 1),
+             perm=empty_i32(rows * k), inv=empty_i32(rows * k), eo=empty_f32(rows * k, d), y=empty_f32(rows, d))
+    q.moe_router_topk(shape, dl_c, x, rows, off, o["idx"], o["w"], None, ws)
+    q.moe_group_by_expert(shape, o["idx"], rows, o["cnt"], o["off"], o["perm"], o["inv"], ws)
+    q.moe_expert_ffn_prefill_chunk(shape, dl_c, x, rows, o["off"], o["perm"], o["eo"], ws)
+    q.moe_combine(shape, dl_c, x, rows, o["eo"], o["inv"], o["w"], o["y"], None, ws)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in o.items()}
+
+
+@pytest.mark.parametrize("rows,zipf", [(48, False), (96, True)], ids=["48rows-uniform", "96rows-zipf"])
+def test_cached_prefill_matches_resident(rows, zipf):
+    """A chunk whose experts outnumber the 16 slots runs in passes (MOE_SLOT_SKIP for the
+    experts of other passes) and gives the resident pool's bits."""
+    shape, slots = synth.GEMMA4, 16
+    k, d, E = shape.top_k, shape.d_model, shape.n_experts
+    L = synth.make_layer(shape, seed=5, layer=0)
+    (resident,) = upload_layers(shape, [L], device())
+    host = HostExpertPool(shape, 1)
+    host.load_layer(0, L)
+    store = TieredStore(host, slots, device())
+    try:
+        cached = store.layer(0, resident.router, resident.shared)
+        off = torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=0)).to(device()) if zipf else None
+        ws = workspace(shape, rows)
+        for chunk in range(2):
+            xd = to_dev_x(synth.make_x(shape, rows, seed=40 + chunk, dtype="bf16"))
+            want = split_prefill(shape, resident.c, xd, rows, off, ws)
+            o = dict(idx=empty_i32(rows, k), w=empty_f32(rows, k), cnt=empty_i32(E), off=empty_i32(E + 1),
+                     perm=empty_i32(rows * k), inv=empty_i32(rows * k), eo=empty_f32(rows * k, d),
+                     y=empty_f32(rows, d))
+            passes, _ = cached.prefill(xd, rows, off, o["idx"], o["w"], o["cnt"], o["off"], o["perm"], o["inv"],
+                                       o["eo"], o["y"], None, ws)
+            torch.cuda.synchronize()
+            got = {n: t.cpu().numpy() for n, t in o.items()}
+            assert passes == -(-int((want["cnt"] > 0).sum()) // slots) and passes >= 2
+            for n in ("idx", "cnt", "perm", "inv"):
+                np.testing.assert_array_equal(got[n], want[n])
+            assert np.array_equal(got["eo"].view(np.uint32), want["eo"].view(np.uint32)), chunk
+            assert np.array_equal(got["y"].view(np.uint32), want["y"].view(np.uint32)), chunk
+        assert q.moe_check_device_error() == 0
+    finally:
+        store.close()
