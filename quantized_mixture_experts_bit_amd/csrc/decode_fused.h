@@ -49,6 +49,7 @@ constexpr int kFusedRows = 16;       // gate/up rows per item
 constexpr int kFusedRouterE = 2;     // experts per router item
 constexpr int kLgCopies = 64;        // copies of the logits ...
 constexpr int kLgStride = 1024;      // ... 8 KiB apart (words)
+constexpr int kLgKeys = 512;         // word of a copy where the ranking keys start
 constexpr int kHCopies = 4;          // copies of h
 constexpr int kSyncLine = 32;        // words per 128-byte line: one sync word per line
 constexpr int kEpochCopies = 64;     // epoch copy c at line c
@@ -73,7 +74,8 @@ struct FusedArgs {
   float* expert_out;    // [top_k][d], unweighted
   float* y;             // [d]
   uint16_t* residual;   // [d] bf16 or null: residual <- bf16(residual + y)
-  uint64_t* lg_tag;     // kLgCopies x kLgStride: fp64 logits as (low, high) 32-bit halves
+  uint64_t* lg_tag;     // kLgCopies x kLgStride: fp64 logits as (low, high) 32-bit halves, then
+                        // at kLgKeys one ranking key per expert (see rank_logits)
   uint64_t* h_tag;      // kHCopies x [(top_k + 1) * fmax] (h_stride apart): GeGLU outputs of the routed
                         // slots, then the shared expert
   uint64_t h_stride;
@@ -247,29 +249,36 @@ __device__ __forceinline__ void stage_x(const XT* __restrict__ x, int d, FusedSm
   }
 }
 
-// Reads the logits (this block's copy) and ranks the experts: S.lg = logits,
-// S.sel_e[0, top_k) = the picks in rank order (logit desc, id asc; NaN as -inf).
-// The ranks are counted on unique 31-bit keys: the top 31 - b bits of the order key
-// above b bits of (E - 1 - id), b = 7 for E <= 128, else 8, so ties go to the lower
-// id. A key beats another when their difference is negative: a subtraction and a
-// shift, independent of each other and summed in four chains (no compare-and-carry
-// chain). That is the true order wherever the truncated parts differ; when two
-// neighbours among ranks 0..top_k share theirs, the ranking is redone on the whole
-// keys (rank_topk). Ends with a barrier.
-__device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
-  const int tid = threadIdx.x, E = F.E, k = F.top_k;
+// The fp64 logits of this block's copy into S.lg and their order keys into S.key
+// (every thread calls this; ends with a barrier).
+__device__ __forceinline__ void load_logits(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
+  const int tid = threadIdx.x, E = F.E;
   const uint64_t* lg = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride;
   poll_tagged<2>([&](int i) { return lg + i; }, 2 * E, tag, [&](int i, uint32_t p) { S.lgw[i] = p; });
   __syncthreads();
-  const int idbits = E <= 128 ? 7 : 8;
   if (tid < E) {
     const double v = __hiloint2double((int)S.lgw[2 * tid + 1], (int)S.lgw[2 * tid]);
-    const uint64_t key = order_key(v);
     S.lg[tid] = v;
-    S.key[tid] = key;
-    S.kp[tid] = ((uint32_t)(key >> (33 + idbits)) << idbits) | (uint32_t)(E - 1 - tid);
+    S.key[tid] = order_key(v);
   }
   __syncthreads();
+}
+
+// Ranks the experts from the ranking keys the router items publish (this block's copy):
+// S.sel_e[0, top_k) = the picks in rank order (logit desc, id asc; NaN as -inf). A key
+// is 32 bits: the top 31 - b bits of the order key above b bits of (E - 1 - id), b = 7
+// for E <= 128, else 8, so keys are unique and ties go to the lower id; a block reads
+// one word per expert instead of the two of an fp64 logit. A key beats another when
+// their difference is negative: a subtraction and a shift, independent of each other
+// and summed in four chains. That is the true order wherever the truncated parts
+// differ; when two neighbours among ranks 0..top_k share theirs, the logits are read
+// in full and the ranking is redone on the whole keys (rank_topk). Ends with a barrier.
+__device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
+  const int tid = threadIdx.x, E = F.E, k = F.top_k;
+  const uint64_t* lk = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride + kLgKeys;
+  poll_tagged<1>([&](int i) { return lk + i; }, E, tag, [&](int i, uint32_t p) { S.kp[i] = p; });
+  __syncthreads();
+  const int idbits = E <= 128 ? 7 : 8;
   // thread t: expert t % E against the competitors of share t / E (256 / E shares of
   // 64, 64 or 16 keys, all of a 32-key run read before the first comparison)
   const int lgE = E == 64 ? 6 : E == 128 ? 7 : 8;
@@ -300,7 +309,10 @@ __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, Fu
   }
   __syncthreads();
   const bool clash = tid < min(k, E - 1) && (S.kp[S.sel_e[tid]] >> idbits) == (S.kp[S.sel_e[tid + 1]] >> idbits);
-  if (__syncthreads_or(clash)) rank_topk(S.key, E, k, S.rank, S.sel_e);
+  if (__syncthreads_or(clash)) {
+    load_logits(F, tag, S);
+    rank_topk(S.key, E, k, S.rank, S.sel_e);
+  }
 }
 
 // The blob of the expert picked for `slot` (nullptr and the error flag if its table
@@ -380,11 +392,20 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
     S.lgv[tid] = l;
   }
   __syncthreads();
-  // 2 words per expert into every copy: thread t stores word t % 4 of copy t / 4
-  if (tid < 2 * kFusedRouterE * kLgCopies) {
-    const int wd = tid % (2 * kFusedRouterE), copy = tid / (2 * kFusedRouterE);
-    const uint64_t bits = (uint64_t)__double_as_longlong(S.lgv[wd >> 1]);
-    put_tag(&F.lg_tag[(size_t)copy * kLgStride + 2 * e0 + wd], (uint32_t)(bits >> (32 * (wd & 1))), tag);
+  // into every copy: the 2 words of each logit, then each expert's ranking key
+  const int idbits = F.E <= 128 ? 7 : 8;
+  constexpr int kWords = 3 * kFusedRouterE;
+  for (int i = tid; i < kWords * kLgCopies; i += 256) {
+    const int wd = i % kWords, copy = i / kWords;
+    uint64_t* dst = F.lg_tag + (size_t)copy * kLgStride;
+    if (wd < 2 * kFusedRouterE) {
+      const uint64_t bits = (uint64_t)__double_as_longlong(S.lgv[wd >> 1]);
+      put_tag(dst + 2 * e0 + wd, (uint32_t)(bits >> (32 * (wd & 1))), tag);
+    } else {
+      const int j = wd - 2 * kFusedRouterE, e = e0 + j;
+      const uint64_t key = order_key(S.lgv[j]);
+      put_tag(dst + kLgKeys + e, ((uint32_t)(key >> (33 + idbits)) << idbits) | (uint32_t)(F.E - 1 - e), tag);
+    }
   }
 }
 
@@ -614,6 +635,7 @@ __device__ __forceinline__ float gather_h(const uint64_t* src, int j0, int j1, u
 __device__ __forceinline__ void pick_weights(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
   const int tid = threadIdx.x, lane = tid & 63, k = F.top_k;
   rank_logits(F, tag, S);
+  load_logits(F, tag, S);  // the picked logits for the weights (long published by now)
   if (tid < 64) {
     const double ex = lane < k ? exp(S.lg[S.sel_e[lane]] - S.lg[S.sel_e[0]]) : 0.0;
     double sum = 0.0;
