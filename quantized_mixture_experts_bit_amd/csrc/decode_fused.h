@@ -47,7 +47,7 @@ namespace qmoe {
 constexpr int kSpinLimit = 1 << 20;  // polling rounds (about a microsecond each) before a wait gives up
 constexpr int kFusedRows = 16;       // gate/up rows per item
 constexpr int kFusedRouterE = 2;     // experts per router item
-constexpr int kLgCopies = 64;        // copies of the logits ...
+constexpr int kLgCopies = 16;        // copies of the logits ...
 constexpr int kLgStride = 1024;      // ... 8 KiB apart (words)
 constexpr int kLgKeys = 512;         // word of a copy where the ranking keys start
 constexpr int kHCopies = 4;          // copies of h
