@@ -88,10 +88,10 @@ struct FusedSmem {
   __attribute__((aligned(16))) uint32_t xb[kFusedXWords];  // x pairs (or values), or h
   float xg[2 * kFusedMaxG];  // sums of x over 32-column halves of each group
   float hsum[48];            // sums of the scaled fp16 h per group
-  float hmax[4];
+  float hmax[4];             // per-wave maxima of |h| (gather_h)
   float red[2][4][64];
   double rd[256];
-  double rd2[32];
+  double rd2[32];            // router: first-level sums of the per-thread partials
   double lg[256];
   uint64_t key[256];
   uint32_t lgw[512];
@@ -266,11 +266,11 @@ __device__ __forceinline__ void load_logits(const FusedArgs& F, uint32_t tag, Fu
 
 // Ranks the experts from the ranking keys the router items publish (this block's copy):
 // S.sel_e[0, top_k) = the picks in rank order (logit desc, id asc; NaN as -inf). A key
-// is 32 bits: the top 31 - b bits of the order key above b bits of (E - 1 - id), b = 7
-// for E <= 128, else 8, so keys are unique and ties go to the lower id; a block reads
-// one word per expert instead of the two of an fp64 logit. A key beats another when
-// their difference is negative: a subtraction and a shift, independent of each other
-// and summed in four chains. That is the true order wherever the truncated parts
+// is a 31-bit value in one word: the top 31 - b bits of the order key above b bits of
+// (E - 1 - id), b = 7 for E <= 128, else 8, so keys are unique and ties go to the lower
+// id; a block reads one word per expert instead of the two of an fp64 logit. As keys
+// are below 2^31, a key beats another when their difference is negative: a subtraction
+// and a shift, independent of each other and summed in four chains. That is the true order wherever the truncated parts
 // differ; when two neighbours among ranks 0..top_k share theirs, the logits are read
 // in full and the ranking is redone on the whole keys (rank_topk). Ends with a barrier.
 __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
