@@ -130,6 +130,13 @@ __device__ __forceinline__ float row16_max(float v) {
   v = dpp_fmax<0x141>(v);  // row_half_mirror
   return dpp_fmax<0x140>(v);  // row_mirror
 }
+// fmaxf over the 64 lanes of a wavefront, the same value in every lane (a NaN is
+// skipped, as fmaxf does): the four row maxima read from lanes 0, 16, 32 and 48
+__device__ __forceinline__ float wave_fmax(float v) {
+  v = row16_max(v);
+  auto lane_f = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  return fmaxf(fmaxf(lane_f(0), lane_f(16)), fmaxf(lane_f(32), lane_f(48)));
+}
 
 // Maximum over the 64 lanes of a wavefront (unsigned), returned to every lane: the
 // DPP steps of wave_sum with max in place of add (rows outside a step's row mask keep

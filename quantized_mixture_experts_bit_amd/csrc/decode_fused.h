@@ -607,11 +607,7 @@ __device__ __forceinline__ float gather_h(const uint64_t* src, int j0, int j1, u
     v[k] = j < j1 ? hf[j] : 0.0f;
     m = fmaxf(m, fabsf(v[k]));  // a NaN is skipped, as fmaxf does
   }
-  m = row16_max(m);
-  m = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0)),
-                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16))),
-            fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32)),
-                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48))));
+  m = wave_fmax(m);
   if (lane == 0) S.hmax[wave] = m;
   __syncthreads();  // also: every fp32 value is read before the fp16 writes below
   const float sc = row_scale(fmaxf(fmaxf(S.hmax[0], S.hmax[1]), fmaxf(S.hmax[2], S.hmax[3])));

@@ -496,12 +496,7 @@ __global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first,
     for (int j = 0; j < kHconvLoads; ++j) v[j] = bld16(hres, (uint32_t)(c0 + 256 * j + 4 * lane) * 4u, 0);
     if (c0 == 0) {
       for (int i = lane; i < nG; i += 64) m = fmaxf(m, mp[i]);
-      // fmaxf over the wavefront (a NaN maximum is skipped, as fmaxf does)
-      m = row16_max(m);
-      m = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0)),
-                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16))),
-                fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 32)),
-                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 48))));
+      m = wave_fmax(m);
     }
     const float sc = row_scale(m);
     if (c0 == 0 && lane == 0) A.hsc[r] = sc;
