@@ -35,6 +35,18 @@ def test_binding_has_the_same_names():
         assert callable(getattr(q, n)), n
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    found = {}
+    for name, val in re.findall(r"#define\s+(MOE_\w+)\s+(0x[0-9A-Fa-f]+|\d+)u?\b", text):
+        found[name] = int(val, 0)
+    for name, val in re.findall(r"\b(MOE_\w+)\s*=\s*(-?\d+)", text):
+        found[name] = int(val)
+    assert {"MOE_OK", "MOE_ERR_DEVICE_CHECK", "MOE_BF16", "MOE_DEVERR_SYNC_TIMEOUT", "MOE_SLOT_SKIP"} <= set(found)
+    for name, val in found.items():
+        assert getattr(q, name) == val, name
+
+
 def test_sizes_match_the_format():
     s = q.MoeShape(2816, 704, 2112)
     # 4.5 bits per weight: codes + one (s, b) bf16 pair per 64 weights
