@@ -121,6 +121,77 @@ def calibrate_copy(mbytes):
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
 
 
+def time_replays(graph, replays, warmup):
+    """Replays `graph` `warmup` times untimed, then `replays` times with a HIP event before
+    each replay and one after the last, all on the current stream (where replay() launches).
+    Returns the per-replay times in ms."""
+    import torch
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for i in range(replays):
+        graph.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(replays)]
+
+
+def spread(per_replay_ms, units):
+    """Median, p10 and p90 of the per-unit time (us) over replays of `units` units each."""
+    import numpy as np
+    v = np.asarray(per_replay_ms, dtype=np.float64) * 1e3 / units
+    return {"median_us": float(np.median(v)), "p10_us": float(np.percentile(v, 10)),
+            "p90_us": float(np.percentile(v, 90)), "replays": int(v.size), "units_per_replay": int(units)}
+
+
+def measured_ceilings(dev):
+    """Achievable rates on this GPU, run as black boxes: a streaming read (torch sum over
+    4 GiB of fp32, far past the 256 MB Infinity Cache) and a large bf16 GEMM (torch matmul,
+    hipBLASLt), each the best of 10 timed runs."""
+    import torch
+    res = {}
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    ts = []
+    for _ in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(a, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    res["stream_read_GBps"] = 4.0 * n / (min(ts[2:]) * 1e-3) / 1e9
+    res["stream_read"] = "torch.sum over 4 GiB of fp32 (read once), best of 10"
+    del a
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    y = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    ts = []
+    for _ in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(x, y)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    res["bf16_gemm_TFLOPs"] = 2.0 * m ** 3 / (min(ts[2:]) * 1e-3) / 1e12
+    res["bf16_gemm"] = "torch.matmul bf16 8192x8192x8192, best of 10"
+    del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
+def flagged_rows(logits, k, gap=1e-4):
+    """Rows whose k-th and (k+1)-th largest logits (the GPU's own fp64 logits) are closer
+    than `gap`: the rows where the picks are a near-tie."""
+    import numpy as np
+    srt = -np.sort(-np.asarray(logits), axis=1)
+    return int(((srt[:, k - 1] - srt[:, k]) < gap).sum())
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +201,7 @@ def main():
     ap.add_argument("--prefill-rows", type=int, default=128)
     ap.add_argument("--stack-rows", type=int, default=256, help="rows per chunk of the 30-layer prefill stack")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the single-layer decode leg (profiling of the others)")
     ap.add_argument("--cache-slots", type=int, default=0,
                     help="also decode through HBM expert slots per layer in front of a pinned host tier (0: off)")
     ap.add_argument("--cache-layers", type=int, default=8, help="layers of the tiered-store decode leg")
@@ -138,6 +210,7 @@ def main():
                     help="also time prefill chunks of these row counts (reported under prefill_chunk_sweep)")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the streaming-read and bf16 GEMM ceilings")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="rows in the oracle's timed CPU sample")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (counter calibration) and exit")
@@ -192,35 +265,38 @@ def main():
     def decode_step(i):
         q.moe_layer_decode(shape, dls[i % L].c, xs[i:i + 1], None, idx[i], w[i], eo, y[i], None, ws)
 
-    # eager pass (also warms up the code objects)
-    for i in range(steps_per_graph):
-        decode_step(i)
-    torch.cuda.synchronize()
-    assert q.moe_check_device_error() == 0
-
-    g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
-    with torch.cuda.graph(g, stream=cap):
+    dbytes = decode_bytes(shape)
+    dec_ms = dec_tok_s = dec_bw = dec_spread = dec_flagged = None
+    dec_steps = 0
+    if not args.no_decode:
+        # eager pass (also warms up the code objects)
         for i in range(steps_per_graph):
             decode_step(i)
-    replays = max(1, args.steps // steps_per_graph)
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(replays):
-        g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    dec_steps = replays * steps_per_graph
-    dec_ms = ev0.elapsed_time(ev1) / dec_steps
-    dec_tok_s = 1000.0 / dec_ms
-    dbytes = decode_bytes(shape)
-    dec_bw = dbytes / (dec_ms * 1e-3)
-    log("decode: %d steps, %.2f us/step, %.0f tok/s, %.2f TB/s on active bytes (%.1f%% of 8 TB/s)"
-        % (dec_steps, dec_ms * 1e3, dec_tok_s, dec_bw / 1e12, 100 * dec_bw / HBM_PEAK))
+        torch.cuda.synchronize()
+        assert q.moe_check_device_error() == 0
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(steps_per_graph):
+                decode_step(i)
+        # at least 10 replays of the whole rotation, whatever --steps asks for
+        replays = max(10, -(-args.steps // steps_per_graph))
+        per_rep = time_replays(g, replays, args.warmup)
+        dec_steps = replays * steps_per_graph
+        dec_ms = sum(per_rep) / dec_steps
+        dec_spread = spread(per_rep, steps_per_graph)
+        # near-ties among the decode rows, from the GPU's own fp64 logits
+        lg_dec = torch.empty(n_x, E, dtype=torch.float64, device=dev)
+        for i in range(steps_per_graph):
+            q.moe_router_topk(shape, dls[i % L].c, xs[i:i + 1], 1, None, idx[i], w[i], lg_dec[i], ws)
+        dec_flagged = flagged_rows(lg_dec.cpu().numpy(), k)
+        dec_tok_s = 1000.0 / dec_ms
+        dec_bw = dbytes / (dec_ms * 1e-3)
+        log("decode: %d steps, %.2f us/step (median %.2f, p10 %.2f, p90 %.2f over %d replays), %.0f tok/s, %.2f TB/s "
+            "on active bytes (%.1f%% of 8 TB/s), %d flagged rows of %d"
+            % (dec_steps, dec_ms * 1e3, dec_spread["median_us"], dec_spread["p10_us"], dec_spread["p90_us"], replays,
+               dec_tok_s, dec_bw / 1e12, 100 * dec_bw / HBM_PEAK, dec_flagged, steps_per_graph))
 
     # ---------------------------------------------------------------- prefill
     def measure_prefill(R):
@@ -254,17 +330,14 @@ def main():
         with torch.cuda.graph(gp, stream=cap):
             for i in range(n_chunks):
                 prefill_step(i)
-        p_replays = max(1, args.steps // 10 // n_chunks)
-        for _ in range(args.warmup):
-            gp.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(p_replays):
-            gp.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        p_ms = e0.elapsed_time(e1) / (p_replays * n_chunks)
+        p_replays = max(10, args.steps // 10 // n_chunks)
+        p_per = time_replays(gp, p_replays, args.warmup)
+        p_ms = sum(p_per) / (p_replays * n_chunks)
+        lgp = torch.empty(R, E, dtype=torch.float64, device=dev)
+        p_flagged = 0
+        for i in range(n_chunks):
+            q.moe_router_topk(shape, dls[i % L].c, xp[i], R, zipf[i % L], pidx[i], pw[i], lgp, wsp)
+            p_flagged += flagged_rows(lgp.cpu().numpy(), k)
         ideal = [prefill_roofline(shape, counts[i], R) for i in range(n_chunks)]
         t_ideal = float(np.mean([t for t, _, _ in ideal]))
         flops = float(np.mean([fl for _, fl, _ in ideal]))
@@ -274,7 +347,8 @@ def main():
             "workload": "prefill chunk of %d rows, same layer shape, Zipf(1.1)-skewed router logits" % R,
             "metric": "MoE-layer tokens/s (prefill chunk %d)" % R,
             "value": R / (p_ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": p_ms,
-            "chunks": p_replays * n_chunks,
+            "chunks": p_replays * n_chunks, "per_chunk": spread(p_per, n_chunks),
+            "flagged_rows": p_flagged, "rows_checked_for_flags": n_chunks * R,
             "roofline": {"bound": "sum over GEMMs of max(bytes/HBM, flops/MFMA)", "ideal_ms": t_ideal * 1e3,
                          "frac": t_ideal / (p_ms * 1e-3)},
             "mfma_util": flops / (p_ms * 1e-3) / MFMA_F16_PEAK,
@@ -319,16 +393,9 @@ def main():
         gsd = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gsd, stream=cap):
             stack_decode()
-        sd_rep = max(2, args.steps // NL)
-        for _ in range(args.warmup):
-            gsd.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(sd_rep):
-            gsd.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        sd_ms = ev0.elapsed_time(ev1) / sd_rep
+        sd_rep = max(20, args.steps // NL)  # at least 20 tokens
+        sd_per = time_replays(gsd, sd_rep, args.warmup)
+        sd_ms = sum(sd_per) / sd_rep
         sd_bytes = NL * dbytes
         # prefill: chunks of RS rows through NL layers, Zipf-skewed routing per layer
         RS = args.stack_rows
@@ -357,16 +424,9 @@ def main():
         gsp = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gsp, stream=cap):
             stack_prefill()
-        sp_rep = max(2, args.steps // 100)
-        for _ in range(args.warmup):
-            gsp.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(sp_rep):
-            gsp.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        sp_ms = ev0.elapsed_time(ev1) / sp_rep
+        sp_rep = max(10, args.steps // 100)  # at least 10 chunks
+        sp_per = time_replays(gsp, sp_rep, args.warmup)
+        sp_ms = sum(sp_per) / sp_rep
         sp_ideal = [prefill_roofline(shape, s_counts[l], RS) for l in range(NL)]
         sp_t = sum(t for t, _, _ in sp_ideal)
         sp_fl = sum(fl for _, fl, _ in sp_ideal)
@@ -378,6 +438,7 @@ def main():
                             "x <- bf16(x + y) between layers; one HIP graph per token" % (NL, E),
                 "metric": "tokens/s through the %d-layer stack (decode bs=1)" % NL,
                 "value": 1000.0 / sd_ms, "unit": "tokens/s", "ms_per_token": sd_ms, "tokens": sd_rep,
+                "per_token": spread(sd_per, 1),
                 "roofline": {"bound": "hbm", "algorithmic_bytes_per_token": sd_bytes,
                              "achieved": sd_bytes / (sd_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                              "frac": sd_bytes / (sd_ms * 1e-3) / HBM_PEAK},
@@ -387,6 +448,7 @@ def main():
                             "in-place residual; one HIP graph per chunk" % (NL, RS),
                 "metric": "tokens/s through the %d-layer stack (prefill chunk %d)" % (NL, RS),
                 "value": RS / (sp_ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": sp_ms, "chunks": sp_rep,
+                "per_chunk": spread(sp_per, 1),
                 "roofline": {"bound": "sum over layers and GEMMs of max(bytes/HBM, flops/MFMA)",
                              "ideal_ms": sp_t * 1e3, "frac": sp_t / (sp_ms * 1e-3)},
                 "mfma_util": sp_fl / (sp_ms * 1e-3) / MFMA_F16_PEAK,
@@ -522,19 +584,38 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        O.set_threads(cores)
+        # the host's share for one GPU: OMP_NUM_THREADS where set (16 on the GPU machines), at most
+        # the logical CPUs the OS reports
+        n_os = os.cpu_count() or 1
+        cores = min(n_os, int(os.environ.get("OMP_NUM_THREADS", n_os)))
         ol = O.OracleLayer(layers_c[0])
         xc = synth.make_x(shape, args.cpu_rows, seed=3, dtype="bf16")
+        O.set_threads(cores)
         t = time.time()
         O.moe_rows(ol, xc, want=("idx", "p", "y"))
         dt = time.time() - t
-        cpu = {"value": args.cpu_rows / dt, "unit": "tokens/s", "cores": O.threads(), "kind": "oracle",
+        used = O.threads()
+        rows1 = max(8, args.cpu_rows // 16)
+        O.set_threads(1)
+        t = time.time()
+        O.moe_rows(ol, xc[:rows1], want=("idx", "p", "y"))
+        dt1 = time.time() - t
+        O.set_threads(cores)
+        cpu = {"value": args.cpu_rows / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
                "sample": "%d independent decode rows of the same layer shape (fp64 C oracle, OpenMP over rows), "
-                         "%.1f s wall" % (args.cpu_rows, dt)}
-        log("cpu oracle: %d rows in %.1f s on %d threads -> %.2f tok/s" % (args.cpu_rows, dt, O.threads(),
-                                                                           cpu["value"]))
+                         "%.1f s wall on %d threads; os.cpu_count() = %d" % (args.cpu_rows, dt, used, n_os),
+               "os_cpu_count": n_os,
+               "single_core": {"value": rows1 / dt1, "unit": "tokens/s", "cores": 1,
+                               "sample": "the first %d of those rows on 1 thread, %.1f s wall" % (rows1, dt1)}}
+        log("cpu oracle: %d rows in %.1f s on %d threads -> %.2f tok/s; %d rows on 1 thread -> %.2f tok/s "
+            "(os.cpu_count() %d)" % (args.cpu_rows, dt, used, cpu["value"], rows1, rows1 / dt1, n_os))
 
+    ceilings = None if args.no_ceilings else measured_ceilings(dev)
+    if ceilings and dec_bw:
+        log("ceilings: streaming read %.0f GB/s, bf16 GEMM %.0f TFLOP/s" % (ceilings["stream_read_GBps"],
+                                                                         ceilings["bf16_gemm_TFLOPs"]))
+        out_frac = dec_bw / (ceilings["stream_read_GBps"] * 1e9)
+        ceilings["decode_frac_of_stream_read"] = out_frac
     traffic, traffic_detail = measured_traffic()
     out = {
         "metric": "MoE-layer tokens/s (decode bs=1)",
@@ -544,6 +625,8 @@ def main():
         "steps": dec_steps,
         "warmup": args.warmup,
         "ms_per_step": dec_ms,
+        "per_step": dec_spread,
+        "flagged_rows": dec_flagged,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -560,15 +643,16 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "k_decode_fused (moe_layer_decode: the whole block for one row in one launch)",
-            "achieved": dec_bw / 1e9,
+            "achieved": dec_bw / 1e9 if dec_bw else None,
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
-            "frac": dec_bw / HBM_PEAK,
+            "frac": dec_bw / HBM_PEAK if dec_bw else None,
             "traffic": traffic,
             "traffic_detail": traffic_detail,
             "algorithmic_bytes_per_launch": dbytes,
         },
         "cpu_baseline": cpu,
+        "measured_ceilings": ceilings,
         "prefill": prefill,
         "stack": stack,
     }

@@ -70,9 +70,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * moe_expert_ffn_prefill_chunk): no flag, its outputs are not written. */
 #define MOE_SLOT_SKIP 0xFFFFFFFFu
 
-/* Shape of one MoE layer. d_model, d_ff, d_ff_shared: multiples of 64;
- * n_experts: multiple of 64, at most 256; 1 <= top_k <= min(n_experts, 16);
- * group must be 64. Gemma-4-26B-A4B-like: {2816, 704, 2112, 128, 8, 64}. */
+/* Shape of one MoE layer. d_model, d_ff, d_ff_shared: multiples of 64, d_model and
+ * d_ff_shared at most 6144; n_experts: 64, 128 or 256; 1 <= top_k <= min(n_experts, 16);
+ * group must be 64; rows * top_k < 65536 per call. Anything else returns
+ * MOE_ERR_UNSUPPORTED_SHAPE. Gemma-4-26B-A4B-like: {2816, 704, 2112, 128, 8, 64}. */
 typedef struct {
   int32_t d_model, d_ff, d_ff_shared, n_experts, top_k, group;
 } moe_shape;
@@ -108,7 +109,10 @@ typedef struct {
 /* Bytes of workspace any entry point below needs for `rows` activation rows. */
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t rows);
 
-/* Zero-fills a workspace (enqueued on `stream`). Required once per workspace. */
+/* Zero-fills a workspace (a hipMemsetAsync enqueued on `stream`). Required once per
+ * workspace, before its first use. Call it outside HIP graph capture: a replayed
+ * memset node would also reset the fused decode's call counter while stale
+ * hand-off words keep their tags. */
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Packed sizes (bytes) of a 4-bit / 8-bit matrix [rows x cols], of one routed
@@ -147,7 +151,13 @@ moe_status moe_unpack_matrix8(const uint8_t* in_host, int32_t rows, int32_t cols
 
 /*
  * Router + top-k + softmax for `rows` rows of x ([rows][d_model], dtype MOE_F32
- * or MOE_BF16, 16-byte aligned):
+ * or MOE_BF16, 16-byte aligned). Defining passages: the router scores every
+ * expert and the top 8 of 128 run per token and layer (blog-mushroom article
+ * "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook", section "Why 26B Fits in
+ * 2 GB"); the router weights stay 8-bit affine while the experts are 4-bit
+ * (rebasdaily article, section "不是把模型塞小，而是边用边取"; ai-heartland review,
+ * section "TurboFieldfareとは", quantisation summary). The pages give no pick
+ * weighting; the softmax over the picked logits is the reading taken here.
  *   logit[r][e] = sum_i (s*q + b)[e][i] * x[r][i] + logit_offset[e]
  * accumulated in fp64 (every product exact), so the top-k set is decided on
  * logits within ~1e-12 of exact. Picks ordered by (logit desc, expert id asc).
@@ -161,7 +171,10 @@ moe_status moe_router_topk(const moe_shape* shape, const moe_layer* layer, const
 
 /*
  * Token-to-expert grouping (prefill): the rows*top_k (row, slot) pairs, pair
- * id = row*top_k + slot, stably sorted by expert id (a counting sort):
+ * id = row*top_k + slot, stably sorted by expert id (a counting sort). It serves
+ * the pages' chunked prefill, where one fetched expert serves every row of the
+ * chunk routed to it (blog-mushroom article, section "Why 26B Fits in 2 GB",
+ * prefill paragraph; paperfeed digest "drumih/turbo-fieldfare", "How it works"):
  *   count [n_experts], offset [n_experts+1] (exclusive prefix sum of count),
  *   perm [rows*top_k] (pair id at each sorted position),
  *   inv_perm [rows*top_k] (sorted position of each pair). Bit-exact.
@@ -177,6 +190,13 @@ moe_status moe_group_by_expert(const moe_shape* shape, const int32_t* topk_idx, 
  * Routed experts for ONE decode row x [d_model]: for each slot j < top_k,
  *   expert_out[j][:] = W_down (gelu_tanh(W_gate x) * (W_up x)) of expert topk_idx[j]
  * (unweighted), fp32 [top_k][d_model]. 4-bit dequant is fused into the GEMVs.
+ * Defining passages: each selected expert's blob runs on the GPU per token
+ * (blog-mushroom article, section "Why 26B Fits in 2 GB", per-token flow); the
+ * experts are MLX affine 4-bit with group 64 and bf16 scale and bias (ai-heartland
+ * review, section "TurboFieldfareとは", quantisation summary). The pages name no
+ * activation; GeGLU with tanh-GELU on the gate is the reading taken here.
+ * topk_idx is device memory [top_k]; ids outside [0, n_experts) or slot entries
+ * outside the pool set the device error word and give zero outputs.
  */
 moe_status moe_expert_ffn_decode(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                                  const int32_t* topk_idx, float* expert_out, void* ws, size_t ws_bytes,
@@ -187,8 +207,13 @@ moe_status moe_expert_ffn_decode(const moe_shape* shape, const moe_layer* layer,
  * (offset, perm from moe_group_by_expert): for sorted position j with pair
  * id p = perm[j], row r = p / top_k, expert e = the expert whose range holds j,
  *   expert_out[j][:] = E_e(x[r]) (unweighted), fp32 [rows*top_k][d_model].
- * Every expert's weights are read once per 64-row tile of its rows and run
- * through MFMA on bf16-dequantized tiles. An expert whose slot-table entry is
+ * Defining passages: prefill runs in chunks of up to 128 rows (256 optional) so
+ * that one fetched expert serves every row routed to it (blog-mushroom article,
+ * section "Why 26B Fits in 2 GB"; paperfeed digest "drumih/turbo-fieldfare",
+ * "How it works"; ai-heartland review, section "OpenAI互換サーバーと、速度に効くつまみ").
+ * Every expert's weights are read once per 64-row tile of its rows; the 4-bit
+ * codes enter the matrix cores exactly and the group scale and bias are applied
+ * per group in fp32 afterwards. An expert whose slot-table entry is
  * MOE_SLOT_SKIP is left out without a flag: the rows of its pairs in expert_out
  * keep their contents. Prefill through an expert cache smaller than a chunk's
  * experts runs this call once per group of resident experts, each pass with a
@@ -201,7 +226,11 @@ moe_status moe_expert_ffn_prefill_chunk(const moe_shape* shape, const moe_layer*
                                         void* stream);
 
 /*
- * Shared expert + weighted combine:
+ * Shared expert + weighted combine. Defining passage: an always-on shared expert
+ * runs beside the routed experts and the two paths merge (blog-mushroom article,
+ * section "Why 26B Fits in 2 GB", per-token flow); the shared expert is one of the
+ * resident weights (same section). The shared expert's weight is 1 and the
+ * routed outputs are weighted by topk_w (the reading taken here):
  *   y[r][:] = S(x[r]) + sum_{j<top_k} topk_w[r][j] * E_j
  * where E_j = expert_out[inv_perm[r*top_k + j]] (prefill, inv_perm != NULL) or
  * expert_out[r*top_k + j] (inv_perm == NULL; decode has rows == 1), summed in
@@ -220,8 +249,12 @@ moe_status moe_combine(const moe_shape* shape, const moe_layer* layer, const voi
 /*
  * Whole block for one decode row, fused: router + top-k + routed experts +
  * shared expert + combine (+ optional residual), the same results as the four
- * calls above. topk_idx/topk_w [top_k], y [d_model]; expert_out [top_k][d_model]
- * receives the unweighted routed outputs.
+ * calls above (the per-token flow of the blog-mushroom article, section "Why 26B
+ * Fits in 2 GB": router, picks, shared expert while the picked experts arrive,
+ * merge). topk_idx/topk_w [top_k], y [d_model]; expert_out [top_k][d_model]
+ * receives the unweighted routed outputs. Runs as one launch when the grid fits
+ * the device at once (the workspace's call counter tags the hand-off words, so the
+ * workspace must not be written between calls), else as three launches.
  */
 moe_status moe_layer_decode(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                             const float* logit_offset, int32_t* topk_idx, float* topk_w, float* expert_out,
@@ -229,9 +262,11 @@ moe_status moe_layer_decode(const moe_shape* shape, const moe_layer* layer, cons
 
 /*
  * Whole block for a prefill chunk: router + top-k, grouping, grouped expert
- * GEMMs, shared expert and combine (+ optional residual). Outputs as the
- * separate calls (with the alignment moe_combine asks for);
- * count/offset/perm/inv_perm as moe_group_by_expert.
+ * GEMMs, shared expert and combine (+ optional residual), the pages' chunked
+ * prefill (blog-mushroom article, section "Why 26B Fits in 2 GB"; paperfeed digest
+ * "drumih/turbo-fieldfare", "How it works"). Outputs as the separate calls (with
+ * the alignment moe_combine asks for); count/offset/perm/inv_perm as
+ * moe_group_by_expert.
  */
 moe_status moe_layer_prefill(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                              int32_t rows, const float* logit_offset, int32_t* topk_idx, float* topk_w,

@@ -18,7 +18,8 @@ __all__ = [
     "moe_expert_blob_bytes", "moe_shared_blob_bytes", "moe_router_blob_bytes",
     "moe_pack_matrix4", "moe_pack_matrix8", "moe_unpack_matrix4", "moe_unpack_matrix8",
     "moe_router_topk", "moe_group_by_expert", "moe_expert_ffn_decode", "moe_expert_ffn_prefill_chunk",
-    "moe_combine", "moe_layer_decode", "moe_layer_prefill", "moe_status_string", "moe_check_device_error",
+    "moe_combine", "moe_layer_decode", "moe_layer_prefill", "moe_status_string",
+    "moe_check_device_error",
     "moe_cache_create", "moe_cache_acquire", "moe_cache_stats", "moe_cache_destroy",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED_SHAPE", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_ERR_DEVICE_CHECK", "MOE_F32", "MOE_BF16", "MOE_DEVERR_BAD_SLOT",

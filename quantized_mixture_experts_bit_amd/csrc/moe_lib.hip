@@ -32,7 +32,8 @@ bool shape_ok(const moe_shape* s) {
   if (s->d_model % 64 || s->d_ff % 64 || s->d_ff_shared % 64) return false;
   // reduction parts of the decode GEMVs: at most 8 of 12 groups each
   if (s->d_model > 8 * kGroupsPerPart * 64 || s->d_ff_shared > 8 * kGroupsPerPart * 64) return false;
-  if (s->n_experts < 64 || s->n_experts > 256 || s->n_experts % 64) return false;
+  // the rankers split the 256 threads of a workgroup evenly over the experts: 64, 128 or 256
+  if (s->n_experts != 64 && s->n_experts != 128 && s->n_experts != 256) return false;
   if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->n_experts) return false;
   return true;
 }
@@ -140,18 +141,16 @@ moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ER
 
 template <typename XT>
 void launch_router(const moe_shape* s, const moe_layer* L, const XT* x, int rows, const float* off, int32_t* idx,
-                   float* w, double* logits, void* ws, hipStream_t st) {
-  const Ws W = ws_layout(s, rows);
+                   float* w, double* logits, void* ws, const Ws& W, hipStream_t st) {
   double* part = at<double>(ws, W.router_partial);
   const int blocks = cdiv(rows, 16) * (s->n_experts / 16) * kRouterSplits;
   k_router_logits<XT><<<blocks, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, part);
   k_router_select<<<rows, 256, 0, st>>>(part, rows, s->n_experts, s->top_k, off, idx, w, logits);
 }
 
-DecodeArgs decode_args(const moe_shape* s, const moe_layer* L, const int32_t* idx, void* ws, float* expert_out,
-                       const float* topk_w, float* y, uint16_t* residual) {
+DecodeArgs decode_args(const moe_shape* s, const moe_layer* L, const int32_t* idx, void* ws, const Ws& W,
+                       float* expert_out, const float* topk_w, float* y, uint16_t* residual) {
   const DecodeCfg dc = decode_cfg(s);
-  const Ws W = ws_layout(s, 1);
   DecodeArgs A;
   memset(&A, 0, sizeof A);
   A.pool = L->pool;
@@ -218,12 +217,12 @@ int fused_capacity() {
 // returns false (nothing launched) otherwise.
 template <typename XT>
 bool launch_decode_fused(const moe_shape* s, const moe_layer* L, const XT* x, const float* off, int32_t* idx,
-                         float* w, float* expert_out, float* y, uint16_t* residual, void* ws, hipStream_t st) {
+                         float* w, float* expert_out, float* y, uint16_t* residual, void* ws, const Ws& W,
+                         hipStream_t st) {
   // limits of the fused kernel's register and LDS tiling (see decode_fused.h)
   const int d = s->d_model, f = s->d_ff, fs = s->d_ff_shared;
   if (d / 64 > kFusedMaxG || f > 64 * 4 * kFusedRoutedGW || fs > 2 * 64 * 4 * kFusedSharedGW) return false;
   if (sizeof(XT) == 4 && d > kFusedXWords) return false;
-  const Ws W = ws_layout(s, 1);
   FusedArgs F;
   memset(&F, 0, sizeof F);
   F.pool = L->pool;
@@ -334,6 +333,26 @@ void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, hipStr
   k_prefill_down<<<persistent_grid(resident_blocks(k_prefill_down, cap_dn), dn_items), 256, 0, st>>>(A);
 }
 
+// The whole block for one decode row with the workspace at `ws` laid out as W: one
+// launch when the grid fits the device at once, else three.
+void layer_decode(const moe_shape* s, const moe_layer* L, const void* x, moe_dtype dt, const float* off, int32_t* idx,
+                  float* w, float* expert_out, float* y, uint16_t* residual, void* ws, const Ws& W, hipStream_t hs) {
+  const bool fused =
+      dt == MOE_BF16 ? launch_decode_fused(s, L, (const uint16_t*)x, off, idx, w, expert_out, y, residual, ws, W, hs)
+                     : launch_decode_fused(s, L, (const float*)x, off, idx, w, expert_out, y, residual, ws, W, hs);
+  if (fused) return;
+  // the grid does not fit on the device at once: three launches instead
+  DecodeArgs A = decode_args(s, L, idx, ws, W, expert_out, w, y, residual);
+  if (dt == MOE_BF16) {
+    launch_router(s, L, (const uint16_t*)x, 1, off, idx, w, nullptr, ws, W, hs);
+    launch_decode_gateup(A, (const uint16_t*)x, true, true, hs);
+  } else {
+    launch_router(s, L, (const float*)x, 1, off, idx, w, nullptr, ws, W, hs);
+    launch_decode_gateup(A, (const float*)x, true, true, hs);
+  }
+  launch_decode_down(A, true, true, true, hs);
+}
+
 }  // namespace
 
 extern "C" {
@@ -370,10 +389,11 @@ moe_status moe_router_topk(const moe_shape* s, const moe_layer* L, const void* x
   if (rows == 0) return MOE_OK;
   if (!idx || !w) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
+  const Ws W = ws_layout(s, rows);
   if (dt == MOE_BF16)
-    launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, logits, ws, hs);
+    launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, logits, ws, W, hs);
   else
-    launch_router(s, L, (const float*)x, rows, off, idx, w, logits, ws, hs);
+    launch_router(s, L, (const float*)x, rows, off, idx, w, logits, ws, W, hs);
   return launched();
 }
 
@@ -399,7 +419,7 @@ moe_status moe_expert_ffn_decode(const moe_shape* s, const moe_layer* L, const v
   if ((st = check_layer(s, L, true, false, false)) != MOE_OK) return st;
   if (!idx || !expert_out) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
-  DecodeArgs A = decode_args(s, L, idx, ws, expert_out, nullptr, nullptr, nullptr);
+  DecodeArgs A = decode_args(s, L, idx, ws, ws_layout(s, 1), expert_out, nullptr, nullptr, nullptr);
   if (dt == MOE_BF16)
     launch_decode_gateup(A, (const uint16_t*)x, true, false, hs);
   else
@@ -437,7 +457,8 @@ moe_status moe_combine(const moe_shape* s, const moe_layer* L, const void* x, mo
   hipStream_t hs = (hipStream_t)stream;
   if (rows == 1 && inv_perm == nullptr) {
     // decode: shared expert as GEMVs, the combine runs in the last workgroup of each output block
-    DecodeArgs A = decode_args(s, L, nullptr, ws, const_cast<float*>(expert_out), topk_w, y, residual);
+    DecodeArgs A = decode_args(s, L, nullptr, ws, ws_layout(s, 1), const_cast<float*>(expert_out), topk_w, y,
+                               residual);
     if (dt == MOE_BF16)
       launch_decode_gateup(A, (const uint16_t*)x, false, true, hs);
     else
@@ -462,21 +483,7 @@ moe_status moe_layer_decode(const moe_shape* s, const moe_layer* L, const void* 
   if (st != MOE_OK) return st;
   if ((st = check_layer(s, L, true, true, true)) != MOE_OK) return st;
   if (!idx || !w || !expert_out || !y) return MOE_ERR_INVALID_ARG;
-  hipStream_t hs = (hipStream_t)stream;
-  const bool fused = dt == MOE_BF16
-                         ? launch_decode_fused(s, L, (const uint16_t*)x, off, idx, w, expert_out, y, residual, ws, hs)
-                         : launch_decode_fused(s, L, (const float*)x, off, idx, w, expert_out, y, residual, ws, hs);
-  if (fused) return launched();
-  // the grid does not fit on the device at once: three launches instead
-  DecodeArgs A = decode_args(s, L, idx, ws, expert_out, w, y, residual);
-  if (dt == MOE_BF16) {
-    launch_router(s, L, (const uint16_t*)x, 1, off, idx, w, nullptr, ws, hs);
-    launch_decode_gateup(A, (const uint16_t*)x, true, true, hs);
-  } else {
-    launch_router(s, L, (const float*)x, 1, off, idx, w, nullptr, ws, hs);
-    launch_decode_gateup(A, (const float*)x, true, true, hs);
-  }
-  launch_decode_down(A, true, true, true, hs);
+  layer_decode(s, L, x, dt, off, idx, w, expert_out, y, residual, ws, ws_layout(s, 1), (hipStream_t)stream);
   return launched();
 }
 
@@ -492,9 +499,9 @@ moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void*
   if (!aligned16(expert_out) || !aligned16(y) || ((uintptr_t)residual & 7u)) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
   if (dt == MOE_BF16)
-    launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, nullptr, ws, hs);
+    launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, nullptr, ws, ws_layout(s, rows), hs);
   else
-    launch_router(s, L, (const float*)x, rows, off, idx, w, nullptr, ws, hs);
+    launch_router(s, L, (const float*)x, rows, off, idx, w, nullptr, ws, ws_layout(s, rows), hs);
   const size_t lds = sizeof(int32_t) * kGroupWaves * s->n_experts;
   k_group<<<1, 1024, lds, hs>>>(idx, rows * s->top_k, s->n_experts, count, offset, perm, inv_perm);
   PrefillArgs A = prefill_args(s, L, rows, offset, perm, expert_out, ws);

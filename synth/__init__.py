@@ -116,6 +116,19 @@ class Variant:
     shared_zero: bool = False       # shared expert with s = b = 0 (contributes exactly 0)
     s_range: tuple = S_RANGE
     b_range: tuple = B_RANGE
+    # Live-stack weights: expert and shared-expert biases centred on the codes' mean
+    # (b' = bf16(b - 7.5 s), so each weight s*q + b' has mean b ~ 0 over q instead of
+    # about +0.09), then s and b' of those matrices multiplied by 2**expert_scale_log2
+    # (exact in bf16). Without a norm between layers the literal weights drive a
+    # 30-layer residual stream into a large common mode (every gate pre-activation
+    # far below 0, so y = 0) or out of fp32 range; these keep it at unit scale.
+    center_bias: bool = False
+    expert_scale_log2: int = 0
+
+
+# the stacked-layer test variant: centred 4-bit biases, experts scaled by 2**-3, and the
+# router's s and b scaled by 2**-6 so that picks 2..k carry weight in the softmax
+LIVE_STACK = Variant(router_scale_log2=-6, center_bias=True, expert_scale_log2=-3)
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -153,16 +166,26 @@ def make_router(shape: MoeShape, seed: int, layer: int, variant: Variant = Varia
     return m
 
 
+def _live(m: QMat, variant: Variant) -> QMat:
+    """A 4-bit matrix under the variant's centring and power-of-two scaling."""
+    if variant.center_bias:
+        s = bf16_bits_to_f32(m.s)
+        m = replace(m, b=f32_to_bf16_bits(bf16_bits_to_f32(m.b) - np.float32(7.5) * s))
+    if variant.expert_scale_log2:
+        m = replace(m, s=_scale_bits(m.s, variant.expert_scale_log2), b=_scale_bits(m.b, variant.expert_scale_log2))
+    return m
+
+
 def make_expert(shape: MoeShape, seed: int, layer: int, e: int, variant: Variant = Variant()) -> Expert:
     d, f = shape.d_model, shape.d_ff
-    mats = [draw_qmat(_rng(seed, layer, KIND_EXPERT, e, j), r, c, 4, variant.s_range, variant.b_range)
+    mats = [_live(draw_qmat(_rng(seed, layer, KIND_EXPERT, e, j), r, c, 4, variant.s_range, variant.b_range), variant)
             for j, (r, c) in enumerate(((f, d), (f, d), (d, f)))]
     return Expert(*mats)
 
 
 def make_shared(shape: MoeShape, seed: int, layer: int, variant: Variant = Variant()) -> Expert:
     d, f = shape.d_model, shape.d_ff_shared
-    mats = [draw_qmat(_rng(seed, layer, KIND_SHARED, 0, j), r, c, 4, variant.s_range, variant.b_range)
+    mats = [_live(draw_qmat(_rng(seed, layer, KIND_SHARED, 0, j), r, c, 4, variant.s_range, variant.b_range), variant)
             for j, (r, c) in enumerate(((f, d), (f, d), (d, f)))]
     if variant.shared_zero:
         mats = [replace(m, s=np.zeros_like(m.s), b=np.zeros_like(m.b)) for m in mats]

@@ -1,13 +1,15 @@
 """Decode through the tiered expert store (HBM slots per layer in front of a pinned host
 pool, moe_cache_*) gives the same bits as decode over the all-resident pool: the same
 kernels run on the same bytes, reached through the cache's slot tables. Checked over a
-stream of tokens that hits, misses and evicts."""
+stream of tokens that hits, misses and evicts. The cached outputs are also checked
+against the fp64 oracle (picks, every unweighted expert output and y)."""
 import numpy as np
 import pytest
 import torch
 
+import oracle as O
 import synth
-from _harness import device, empty_f32, empty_i32, to_dev_x, workspace
+from _harness import REL_TOL, check_topk, device, empty_f32, empty_i32, rel_err, to_dev_x, workspace
 
 pytestmark = pytest.mark.gpu
 q = pytest.importorskip("quantized_mixture_experts_bit_amd")
@@ -46,15 +48,25 @@ def test_cached_decode_matches_resident(shape, slots, zipf):
                 for l in range(n_layers)]
         ws = workspace(shape, 1)
         total_miss = 0
+        olayers = [O.OracleLayer(L) for L in layers]
         for t in range(tokens):
             for l in range(n_layers):
-                x = to_dev_x(synth.make_x(shape, 1, seed=100 + t, stream=l, dtype="bf16"))
+                x_np = synth.make_x(shape, 1, seed=100 + t, stream=l, dtype="bf16")
+                x = to_dev_x(x_np)
                 i0, e0, y0, _ = decode_split(shape, resident[l].c, x, offs[l], ws)
                 i1, e1, y1, miss = decode_split(shape, cached[l].c, x, offs[l], ws, cached[l])
                 np.testing.assert_array_equal(i1, i0)
                 assert np.array_equal(e1.view(np.uint32), e0.view(np.uint32)), (t, l)
                 assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32)), (t, l)
                 total_miss += miss
+                # the cached outputs against the oracle
+                off_np = None if offs[l] is None else offs[l].cpu().numpy()
+                ref = O.moe_rows(olayers[l], x_np, offset=off_np)
+                if check_topk(i1[None], ref, shape.top_k)[0]:
+                    ref = O.moe_rows(olayers[l], x_np, offset=off_np, idx=i1[None])
+                assert rel_err(y1, ref["y"][0]) <= REL_TOL, (t, l)
+                for j in range(shape.top_k):
+                    assert rel_err(e1[j], ref["expert_out"][0, j]) <= REL_TOL, (t, l, j)
         assert q.moe_check_device_error() == 0
         hits, misses, nbytes = store.stats()
         assert hits + misses == tokens * n_layers * shape.top_k
@@ -96,8 +108,10 @@ def test_cached_prefill_matches_resident(rows, zipf):
         cached = store.layer(0, resident.router, resident.shared)
         off = torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=0)).to(device()) if zipf else None
         ws = workspace(shape, rows)
+        ol = O.OracleLayer(L)
         for chunk in range(2):
-            xd = to_dev_x(synth.make_x(shape, rows, seed=40 + chunk, dtype="bf16"))
+            x_np = synth.make_x(shape, rows, seed=40 + chunk, dtype="bf16")
+            xd = to_dev_x(x_np)
             want = split_prefill(shape, resident.c, xd, rows, off, ws)
             o = dict(idx=empty_i32(rows, k), w=empty_f32(rows, k), cnt=empty_i32(E), off=empty_i32(E + 1),
                      perm=empty_i32(rows * k), inv=empty_i32(rows * k), eo=empty_f32(rows * k, d),
@@ -111,6 +125,16 @@ def test_cached_prefill_matches_resident(rows, zipf):
                 np.testing.assert_array_equal(got[n], want[n])
             assert np.array_equal(got["eo"].view(np.uint32), want["eo"].view(np.uint32)), chunk
             assert np.array_equal(got["y"].view(np.uint32), want["y"].view(np.uint32)), chunk
+            # every row of the cached chunk against the oracle
+            off_np = None if off is None else off.cpu().numpy()
+            ref = O.moe_rows(ol, x_np, offset=off_np)
+            if check_topk(got["idx"], ref, k).any():
+                ref = O.moe_rows(ol, x_np, offset=off_np, idx=got["idx"])
+            for r in range(rows):
+                assert rel_err(got["y"][r], ref["y"][r]) <= REL_TOL, (chunk, r)
+                for j in range(k):
+                    pos = got["inv"][r * k + j]
+                    assert rel_err(got["eo"][pos], ref["expert_out"][r, j]) <= REL_TOL, (chunk, r, j)
         assert q.moe_check_device_error() == 0
     finally:
         store.close()

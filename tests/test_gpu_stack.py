@@ -7,18 +7,26 @@ buffer are one tensor):
   - decode: one row through the 30 blocks;
   - prefill: chunks of 256 rows with Zipf-skewed routing through the 30 blocks.
 
-The oracle runs its own 30-layer chains from the same x_0 (its fp64 block
-outputs, its own residual rounding); no GPU value is fed to it. As written, the
-stacks are degenerate after the first layer: the residual gains a large common
-mode, and on most rows every gate pre-activation becomes very negative,
-tanh-GELU is exactly 0 and y is exactly 0 from then on, on both sides; on some
-rows the common mode has the other sign and the row overflows to inf/NaN within
-a few layers. So the chains are compared layer by layer (y within the tolerance,
-the bf16 residual within one ulp) while a row stays within fp32 range, the
-non-trivial numerics are carried by the first layers and by the single-layer
-tests, and the routing must stay valid on every row and layer. Two properties of the GPU path are checked as well: the residual store
-equals RNE_bf16(RNE_fp32(x + y)) of the call's own x and y, and a HIP graph of the
-whole stack replays to the same bits as the eager calls.
+Parity is checked teacher-forced: after the GPU has run layer l, the oracle
+runs layer l on the GPU's own bf16 input x_l and the layer's outputs are
+compared (the picks exactly on unflagged rows, y and the unweighted expert
+outputs within the tolerance; flagged rows through the conditional oracle at the
+GPU's picks). The residual store is checked bit-exact against RNE_bf16(RNE_fp32(
+x_l + y_l)) of the GPU's own x_l and y_l.
+
+Two stacks run:
+  - literal: the workload weights. Without a norm between layers the residual
+    stream gains a large common mode after the first layer: on most rows every
+    gate pre-activation is then far below zero, tanh-GELU is exactly 0 and y is
+    exactly 0; on some rows the common mode has the other sign and the row
+    leaves fp32 range within a few layers. Layers whose input is finite are
+    still compared, but they carry little numerics;
+  - live (synth.LIVE_STACK, test-only weights): expert biases centred on the
+    codes' mean and the experts scaled by 2^-3, the router by 2^-6. The residual
+    stream stays near unit scale over all 30 layers, every gate is live and
+    picks 2..k carry weight, so every layer of both stacks is checked on
+    non-trivial values.
+A HIP graph of the whole literal stack replays to the same bits as the eager calls.
 """
 import numpy as np
 import pytest
@@ -26,14 +34,14 @@ import torch
 
 import oracle as O
 import synth
-from _harness import REL_TOL, check_topk, device, empty_f32, empty_i32, rel_err, to_dev_x, workspace
+from _harness import FLAG_GAP, REL_TOL, check_topk, device, empty_f32, empty_i32, rel_err, to_dev_x, workspace
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 q = pytest.importorskip("quantized_mixture_experts_bit_amd")
 
 N_LAYERS = 30
 PF_ROWS = 256
-PF_SAMPLE = np.array([0, 101, 255])  # rows whose chains the oracle follows
+PF_SAMPLE = np.array([0, 37, 101, 128, 200, 255])  # prefill rows the oracle evaluates in full on every layer
 
 
 def bf16_bits(t):
@@ -48,16 +56,17 @@ def residual_property(x_bits, y):
     return u.astype(np.uint16)
 
 
-def ulp_diff_bf16(a, b):
-    """|a - b| in bf16 ulps for finite values of equal sign class (ordered ints)."""
-    def ordered(v):
-        v = v.astype(np.int32)
-        return np.where(v & 0x8000, 0x8000 - (v & 0x7FFF), v + 0x8000)
-    return np.abs(ordered(a) - ordered(b))
+def is_nan_bf16(v):
+    return ((v & 0x7F80) == 0x7F80) & ((v & 0x007F) != 0)
 
 
-@pytest.fixture(scope="module")
-def stack():
+def finite_rows(x_bits):
+    return np.all((x_bits & 0x7F80) != 0x7F80, axis=-1)
+
+
+def run_stack(variant, zipf_sigma_scale):
+    """Runs both stacks layer by layer on the GPU and the oracle teacher-forced on each
+    layer's GPU input. Returns the per-layer records and the device state."""
     from quantized_mixture_experts_bit_amd.weights import ExpertPool
     shape = synth.GEMMA4
     E, k, d = shape.n_experts, shape.top_k, shape.d_model
@@ -71,12 +80,12 @@ def stack():
     pf = dict(idx=empty_i32(PF_ROWS, k), w=empty_f32(PF_ROWS, k), cnt=empty_i32(E), off=empty_i32(E + 1),
               perm=empty_i32(PF_ROWS * k), inv=empty_i32(PF_ROWS * k), eo=empty_f32(PF_ROWS * k, d),
               y=empty_f32(PF_ROWS, d))
-    xo_dec, xo_pf = x0_dec.copy(), x0_pf[PF_SAMPLE].copy()  # the oracle's own chains
+    sigma = synth.router_logit_std(shape) * 2.0 ** variant.router_scale_log2 * zipf_sigma_scale
     layers, zipf, rec = [], [], []
     for l in range(N_LAYERS):
-        L = synth.make_layer(shape, seed=0, layer=l)
+        L = synth.make_layer(shape, seed=0, layer=l, variant=variant)
         dl = pool.add_layer(L, l * E)
-        zo = synth.make_zipf_offset(shape, seed=0, layer=l)
+        zo = synth.make_zipf_offset(shape, seed=0, layer=l, sigma=sigma)
         zd = torch.from_numpy(zo).to(dev)
         layers.append(dl)
         zipf.append(zd)
@@ -85,96 +94,166 @@ def stack():
         q.moe_layer_prefill(shape, dl.c, h_pf, PF_ROWS, zd, pf["idx"], pf["w"], pf["cnt"], pf["off"], pf["perm"],
                             pf["inv"], pf["eo"], pf["y"], h_pf, ws_pf)
         torch.cuda.synchronize()
+        g = dict(dec=dict(idx=idx_d.cpu().numpy(), w=w_d.cpu().numpy(), eo=eo_d.cpu().numpy()[None],
+                          y=y_d.cpu().numpy(), x=xin_d, h=bf16_bits(h_dec), rows=np.array([0])),
+                 pf=dict(idx=pf["idx"].cpu().numpy(), w=pf["w"].cpu().numpy(), cnt=pf["cnt"].cpu().numpy(),
+                         perm=pf["perm"].cpu().numpy(), inv=pf["inv"].cpu().numpy(), y=pf["y"].cpu().numpy(),
+                         x=xin_p, h=bf16_bits(h_pf), rows=PF_SAMPLE))
+        eo_pf = pf["eo"].cpu().numpy()
+        g["pf"]["eo"] = np.stack([eo_pf[g["pf"]["inv"][r * k:(r + 1) * k]] for r in PF_SAMPLE])
         ol = O.OracleLayer(L)
-        ref_d = O.moe_rows(ol, xo_dec, want=("logits", "idx", "p", "gap", "y"))
-        ref_p = O.moe_rows(ol, xo_pf, offset=zo, want=("logits", "idx", "p", "gap", "y"))
-        rec.append(dict(
-            dec=dict(x_gpu=xin_d, x_orc=xo_dec.copy(), y=y_d.cpu().numpy(), idx=idx_d.cpu().numpy(),
-                     h=bf16_bits(h_dec), ref=ref_d),
-            pf=dict(x_gpu=xin_p, x_orc=xo_pf.copy(), y=pf["y"].cpu().numpy(), idx=pf["idx"].cpu().numpy(),
-                    h=bf16_bits(h_pf), ref=ref_p)))
-        xo_dec = O.residual_bf16(xo_dec, ref_d["y"])
-        xo_pf = O.residual_bf16(xo_pf, ref_p["y"])
+        # teacher-forced: the oracle runs this layer on the GPU's own input rows
+        for key, off in (("dec", None), ("pf", zo)):
+            c = g[key]
+            xs = c["x"][c["rows"]]
+            ref = O.moe_rows(ol, xs, offset=off)
+            flagged = ref["gap"] < FLAG_GAP
+            c["ref"] = ref
+            c["ref_cond"] = O.moe_rows(ol, xs, offset=off, idx=c["idx"][c["rows"]]) if flagged.any() else None
+        # the picks of every prefill row against the oracle's router on the GPU's input
+        lg = O.router_logits(L, g["pf"]["x"], offset=zo)
+        tk = [O.topk_softmax(lg[r], k) for r in range(PF_ROWS)]
+        g["pf"]["ref_all"] = dict(idx=np.stack([t[0] for t in tk]), gap=np.array([t[2] for t in tk]), logits=lg)
+        rec.append(g)
+        print("stack %s: layer %d done" % ("live" if variant.center_bias else "literal", l), flush=True)
         del L, ol
     assert q.moe_check_device_error() == 0
     return dict(shape=shape, layers=layers, zipf=zipf, rec=rec, x0_dec=x0_dec, x0_pf=x0_pf, ws_dec=ws_dec,
                 ws_pf=ws_pf, pf=pf, dec=(idx_d, w_d, eo_d, y_d), pool=pool)
 
 
-FP32_SAFE = 1e30  # the oracle's fp64 values beyond this no longer fit the GPU's fp32 path
+@pytest.fixture(scope="module")
+def literal():
+    return run_stack(synth.Variant(), 1.0)
 
 
-def _check_chain(rec, key, rows_gpu):
-    """Layer-by-layer comparison of the GPU chain with the oracle's own chain, for
-    each row as long as the oracle's input and output stay finite and within fp32
-    range (some rows of the literal stacks overflow within a few layers); returns
-    the number of (row, layer) pairs compared."""
-    k = synth.GEMMA4.top_k
-    live = np.ones(len(rows_gpu), dtype=bool)
+@pytest.fixture(scope="module")
+def live():
+    return run_stack(synth.LIVE_STACK, 1.0)
+
+
+def check_layer(c, l, key, k):
+    """One layer's outputs against the oracle evaluated on the GPU's input. Returns the
+    number of rows compared (rows whose input is finite and whose oracle output fits fp32)."""
     compared = 0
-    for l, r in enumerate(rec):
-        c = r[key]
+    xs = c["x"][c["rows"]]
+    ok = finite_rows(xs)
+    for i, r in enumerate(c["rows"]):
         ref = c["ref"]
-        xo = O.x_to_f64(c["x_orc"])
-        for i, row in enumerate(rows_gpu):
-            if live[i] and not (np.all(np.isfinite(xo[i])) and np.all(np.isfinite(ref["y"][i]))
-                                and np.abs(ref["y"][i]).max() < FP32_SAFE):
-                live[i] = False
-            if not live[i]:
-                continue
-            # the two chains' inputs to layer l agree within one bf16 ulp
-            assert ulp_diff_bf16(c["x_gpu"][row], c["x_orc"][i]).max() <= 1, "layer %d row %d: inputs" % (l, row)
-            sub = {n: (v[i:i + 1] if v is not None else None) for n, v in ref.items()}
-            flagged = check_topk(c["idx"][row][None], sub, k)
-            assert not flagged.any(), "layer %d row %d: a near-tie, the chains may legitimately part" % (l, row)
-            if np.abs(ref["y"][i]).max() == 0.0:
-                assert np.all(c["y"][row] == 0.0), "layer %d row %d: oracle y is 0, GPU is not" % (l, row)
-            else:
-                assert rel_err(c["y"][row], ref["y"][i]) <= REL_TOL, "layer %d row %d" % (l, row)
-            compared += 1
+        if not ok[i] or not np.all(np.abs(ref["y"][i]) < 1e30):
+            continue
+        sub = {n: (v[i:i + 1] if v is not None else None) for n, v in ref.items()}
+        if check_topk(c["idx"][r][None], sub, k)[0]:
+            ref, i_ref = c["ref_cond"], i  # flagged: the oracle at the GPU's picks
+        else:
+            i_ref = i
+        y_ref = ref["y"][i_ref]
+        if np.abs(y_ref).max() == 0.0:
+            assert np.all(c["y"][r] == 0.0), "%s layer %d row %d: oracle y is 0, GPU is not" % (key, l, r)
+        else:
+            e = rel_err(c["y"][r], y_ref)
+            assert e <= REL_TOL, "%s layer %d row %d: y %.3g" % (key, l, r, e)
+        # each pick's weight and unweighted output, matched by expert id (the order inside
+        # the set may differ only where two picked logits tie)
+        slot_of = {int(e): j for j, e in enumerate(ref["idx"][i_ref])}
+        for j, e in enumerate(c["idx"][r]):
+            jr = slot_of[int(e)]
+            assert abs(float(c["w"][r][j]) - ref["p"][i_ref, jr]) <= 1e-6, \
+                "%s layer %d row %d expert %d: weight %g vs %g" % (key, l, r, e, c["w"][r][j], ref["p"][i_ref, jr])
+            eo_ref = ref["expert_out"][i_ref, jr]
+            if np.abs(eo_ref).max() > 0.0:
+                err = rel_err(c["eo"][i, j], eo_ref)
+                assert err <= REL_TOL, "%s layer %d row %d expert %d: %.3g" % (key, l, r, e, err)
+        compared += 1
     return compared
 
 
-def test_stack_decode_matches_oracle_chain(stack):
-    assert _check_chain(stack["rec"], "dec", np.array([0])) >= 2
+@pytest.mark.parametrize("key", ["dec", "pf"])
+def test_live_stack_teacher_forced_every_layer(live, key):
+    """All 30 layers of the live stack: picks, weights, y and every unweighted expert
+    output of the decode row and the sampled prefill rows, on non-trivial values."""
+    k = synth.GEMMA4.top_k
+    total = 0
+    for l, g in enumerate(live["rec"]):
+        c = g[key]
+        n = check_layer(c, l, key, k)
+        assert n == len(c["rows"]), "%s layer %d: only %d of %d rows compared" % (key, l, n, len(c["rows"]))
+        total += n
+        # the layer is live: y is a real fraction of the residual stream on every checked row
+        xs = O.x_to_f64(c["x"][c["rows"]])
+        ys = c["y"][c["rows"]]
+        assert np.all(np.abs(ys).max(axis=1) > 0.05 * np.sqrt((xs ** 2).mean(axis=1))), "%s layer %d" % (key, l)
+    assert total == N_LAYERS * len(live["rec"][0][key]["rows"])
 
 
-def test_stack_prefill_matches_oracle_chain(stack):
-    assert _check_chain(stack["rec"], "pf", PF_SAMPLE) >= 2 * len(PF_SAMPLE)
+@pytest.mark.parametrize("which", ["literal", "live"])
+def test_stack_prefill_picks_every_row(request, which):
+    """The picks of all 256 rows on every layer against the oracle's router on the GPU's
+    input (bit-exact sets and order on unflagged rows), and the grouping of those picks."""
+    st = request.getfixturevalue(which)
+    k, E = synth.GEMMA4.top_k, synth.GEMMA4.n_experts
+    checked = 0
+    for l, g in enumerate(st["rec"]):
+        c = g["pf"]
+        fin = finite_rows(c["x"])
+        ra = c["ref_all"]
+        for r in np.flatnonzero(fin):
+            sub = dict(idx=ra["idx"][r:r + 1], gap=ra["gap"][r:r + 1], logits=ra["logits"][r:r + 1])
+            check_topk(c["idx"][r][None], sub, k)
+            checked += 1
+        rc, ro, rp, ri = O.group_by_expert(c["idx"], E)
+        np.testing.assert_array_equal(c["cnt"], rc, err_msg="layer %d" % l)
+        np.testing.assert_array_equal(c["perm"], rp, err_msg="layer %d" % l)
+        np.testing.assert_array_equal(c["inv"], ri, err_msg="layer %d" % l)
+    if which == "live":
+        assert checked == N_LAYERS * PF_ROWS
 
 
-def test_stack_routing_stays_valid(stack):
-    """Whatever the activations hold (the literal stacks overflow on some rows),
+def test_live_stack_prefill_routing_is_skewed(live):
+    """The Zipf offset makes experts repeat across the 256 rows on every layer."""
+    for l, g in enumerate(live["rec"]):
+        cnt = g["pf"]["cnt"]
+        assert (cnt > 0).sum() < 90 and cnt.max() >= 64, "layer %d: %d experts, busiest %d" % (
+            l, (cnt > 0).sum(), cnt.max())
+
+
+@pytest.mark.parametrize("key", ["dec", "pf"])
+def test_literal_stack_teacher_forced(literal, key):
+    """Every layer of the literal stack whose input is finite, against the oracle on the
+    GPU's input; the first layer carries real numerics."""
+    k = synth.GEMMA4.top_k
+    total = sum(check_layer(g[key], l, key, k) for l, g in enumerate(literal["rec"]))
+    print("literal stack, %s: %d (row, layer) pairs compared" % (key, total))
+    assert total >= N_LAYERS
+    assert np.abs(literal["rec"][0][key]["y"]).max() > 1.0
+
+
+@pytest.mark.parametrize("which", ["literal", "live"])
+def test_stack_routing_stays_valid(request, which):
+    """Whatever the activations hold (the literal stack leaves fp32 range on some rows),
     every layer's picks are k distinct valid expert ids on every row."""
+    st = request.getfixturevalue(which)
     E, k = synth.GEMMA4.n_experts, synth.GEMMA4.top_k
-    for l, r in enumerate(stack["rec"]):
+    for l, r in enumerate(st["rec"]):
         for key in ("dec", "pf"):
             idx = r[key]["idx"].reshape(-1, k)
             assert idx.min() >= 0 and idx.max() < E, "layer %d %s" % (l, key)
             assert all(len(set(row.tolist())) == k for row in idx), "layer %d %s" % (l, key)
 
 
-def test_stack_first_layer_is_not_trivial(stack):
-    """Layer 0 carries real numerics on both paths (later layers may be exactly zero)."""
-    for key in ("dec", "pf"):
-        assert np.abs(stack["rec"][0][key]["y"]).max() > 1.0
-        assert np.abs(stack["rec"][0][key]["ref"]["y"]).max() > 1.0
-
-
-def is_nan_bf16(v):
-    return ((v & 0x7F80) == 0x7F80) & ((v & 0x007F) != 0)
-
-
+@pytest.mark.parametrize("which", ["literal", "live"])
 @pytest.mark.parametrize("key", ["dec", "pf"])
-def test_stack_residual_store_property(stack, key):
-    for l, r in enumerate(stack["rec"]):
+def test_stack_residual_store_property(request, which, key):
+    st = request.getfixturevalue(which)
+    for l, r in enumerate(st["rec"]):
         c = r[key]
-        exp = residual_property(c["x_gpu"], c["y"])
+        exp = residual_property(c["x"], c["y"])
         same = (c["h"] == exp) | (is_nan_bf16(c["h"]) & is_nan_bf16(exp))  # NaN payloads may differ
         assert same.all(), "layer %d" % l
 
 
-def test_stack_decode_graph_replay_bit_exact(stack):
+def test_stack_decode_graph_replay_bit_exact(literal):
+    stack = literal
     shape, layers = stack["shape"], stack["layers"]
     idx_d, w_d, eo_d, y_d = stack["dec"]
     h = torch.empty(1, shape.d_model, dtype=torch.bfloat16, device=device())
@@ -200,7 +279,8 @@ def test_stack_decode_graph_replay_bit_exact(stack):
     assert q.moe_check_device_error() == 0
 
 
-def test_stack_prefill_graph_replay_bit_exact(stack):
+def test_stack_prefill_graph_replay_bit_exact(live):
+    stack = live
     shape, layers, zipf, pf = stack["shape"], stack["layers"], stack["zipf"], stack["pf"]
     h = torch.empty(PF_ROWS, shape.d_model, dtype=torch.bfloat16, device=device())
     x0 = to_dev_x(stack["x0_pf"])

@@ -128,6 +128,9 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert _call_router(q.MoeShape(2800, 704, 2112)) == q.MOE_ERR_UNSUPPORTED_SHAPE
     assert _call_router(q.MoeShape(2816, 700, 2112)) == q.MOE_ERR_UNSUPPORTED_SHAPE
     assert _call_router(q.MoeShape(2816, 704, 2112, n_experts=96)) == q.MOE_ERR_UNSUPPORTED_SHAPE
+    # a multiple of 64 that does not divide the rankers' 256 threads evenly
+    assert _call_router(q.MoeShape(2816, 704, 2112, n_experts=192)) == q.MOE_ERR_UNSUPPORTED_SHAPE
+    assert _call_router(q.MoeShape(2816, 704, 2112, n_experts=320)) == q.MOE_ERR_UNSUPPORTED_SHAPE
     assert _call_router(q.MoeShape(2816, 704, 2112, top_k=0)) == q.MOE_ERR_UNSUPPORTED_SHAPE
     assert _call_router(q.MoeShape(2816, 704, 2112, top_k=17)) == q.MOE_ERR_UNSUPPORTED_SHAPE
     assert _call_router(q.MoeShape(2816, 704, 2112, group=32)) == q.MOE_ERR_UNSUPPORTED_SHAPE
