@@ -261,6 +261,30 @@ moe_status moe_layer_decode(const moe_shape* shape, const moe_layer* layer, cons
                             float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace: its scratch is a static device array of the library (4 MiB per GPU the
+ * library runs on, held until the process ends), found once per device with
+ * hipGetSymbolAddress. It calls no hipMalloc, hipFree or allocating routine. Same
+ * arguments and results as moe_layer_decode without ws/ws_bytes; the caller still
+ * owns every input and output.
+ *   - Shapes past the scratch's maximum (d_model 3072, d_ff 768, d_ff_shared 2560,
+ *     n_experts 256, top_k 16) return MOE_ERR_WORKSPACE and launch nothing.
+ *   - Every call on one GPU shares that GPU's scratch and finds it as the previous
+ *     call left it: calls that overlap in time on one GPU (several streams or host
+ *     threads at once) race and give wrong results. Calls in stream order are safe,
+ *     for any mix of shapes.
+ *   - The first call on a device enqueues a clear of the scratch (a fill kernel) on
+ *     `stream` before its work; a call captured into a HIP graph before any
+ *     uncaptured call has cleared it captures the clear too, so each replay starts
+ *     clean. After moe_check_device_error reports MOE_DEVERR_SYNC_TIMEOUT, the next
+ *     call clears it again.
+ */
+moe_status moe_layer_decode_noalloc(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
+                                    const float* logit_offset, int32_t* topk_idx, float* topk_w, float* expert_out,
+                                    float* y, uint16_t* residual_bf16, void* stream);
+
+/*
  * Whole block for a prefill chunk: router + top-k, grouping, grouped expert
  * GEMMs, shared expert and combine (+ optional residual), the pages' chunked
  * prefill (blog-mushroom article, section "Why 26B Fits in 2 GB"; paperfeed digest

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "decode_fused.h"
@@ -17,8 +18,13 @@
 
 using namespace qmoe;
 
+// Decode workspace of moe_layer_decode_noalloc (see "static scratch" below).
+constexpr size_t kStaticScratchBytes = 4u << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
 
+constexpr int kMaxDevices = 64;
 constexpr int kDecodeGW = 3;      // groups per wavefront per load batch in the decode GEMVs
 constexpr int kGroupsPerPart = 12;  // reduction groups per decode workgroup
 
@@ -353,6 +359,75 @@ void layer_decode(const moe_shape* s, const moe_layer* L, const void* x, moe_dty
   launch_decode_down(A, true, true, true, hs);
 }
 
+// ------------------------------------------------------------------ static scratch (moe_layer_decode_noalloc)
+
+// The decode workspace of moe_layer_decode_noalloc, in the library's own device memory.
+// Its layout is the one of the largest shape that entry point takes, so every region
+// sits at the same offset for every shape: the counters (zero between calls) and the
+// call counter of the fused decode keep their places, tagged hand-off words of any
+// earlier call carry older tags, and scratch regions of one shape never overlap the
+// tagged regions of another. Host code never passes `scratch` itself to a kernel: it
+// passes the address hipGetSymbolAddress returns for the current device.
+const moe_shape kStaticMaxShape = {3072, 768, 2560, 256, 16, 64};
+
+const Ws& static_layout() {
+  static const Ws W = ws_layout(&kStaticMaxShape, 1);
+  return W;
+}
+
+bool static_shape_ok(const moe_shape* s) {
+  return s->d_model <= kStaticMaxShape.d_model && s->d_ff <= kStaticMaxShape.d_ff &&
+         s->d_ff_shared <= kStaticMaxShape.d_ff_shared && s->n_experts <= kStaticMaxShape.n_experts &&
+         s->top_k <= kStaticMaxShape.top_k && static_layout().total <= kStaticScratchBytes;
+}
+
+__global__ __launch_bounds__(256) void k_zero16(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchState {
+  void* ptr;     // device address of `scratch` on this device
+  bool cleared;  // a clear has been enqueued outside graph capture
+};
+std::mutex g_scratch_mu;
+ScratchState g_scratch[kMaxDevices];
+
+// The current device's scratch address (looked up once per device, with that device
+// current). The first call on a device enqueues a clear on `st`; so does every call
+// made under graph capture until one outside capture has cleared it (a captured clear
+// runs only when the graph is replayed). A clear covers the whole scratch, so a graph
+// holding one starts every replay from a clean state.
+moe_status static_scratch(hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState& S = g_scratch[dev];
+  if (!S.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    S.ptr = p;
+  }
+  if (!S.cleared) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) return MOE_ERR_HIP;
+    k_zero16<<<256, 256, 0, st>>>((uint4*)S.ptr, kStaticScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    if (cap == hipStreamCaptureStatusNone) S.cleared = true;
+  }
+  *out = S.ptr;
+  return MOE_OK;
+}
+
+// After a fused-decode wait gave up, the current device's scratch is cleared again
+// before its next use.
+void static_scratch_invalidate() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch[dev].cleared = false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -487,6 +562,23 @@ moe_status moe_layer_decode(const moe_shape* s, const moe_layer* L, const void* 
   return launched();
 }
 
+moe_status moe_layer_decode_noalloc(const moe_shape* s, const moe_layer* L, const void* x, moe_dtype dt,
+                                    const float* off, int32_t* idx, float* w, float* expert_out, float* y,
+                                    uint16_t* residual, void* stream) {
+  if (!shape_ok(s)) return s ? MOE_ERR_UNSUPPORTED_SHAPE : MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!x || !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  if (!static_shape_ok(s)) return MOE_ERR_WORKSPACE;  // past what the static scratch holds
+  moe_status st = check_layer(s, L, true, true, true);
+  if (st != MOE_OK) return st;
+  if (!idx || !w || !expert_out || !y) return MOE_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  void* scratch_ptr = nullptr;
+  if ((st = static_scratch(hs, &scratch_ptr)) != MOE_OK) return st;
+  layer_decode(s, L, x, dt, off, idx, w, expert_out, y, residual, scratch_ptr, static_layout(), hs);
+  return launched();
+}
+
 moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void* x, moe_dtype dt, int32_t rows,
                              const float* off, int32_t* idx, float* w, int32_t* count, int32_t* offset,
                              int32_t* perm, int32_t* inv_perm, float* expert_out, float* y, uint16_t* residual,
@@ -533,6 +625,7 @@ moe_status moe_check_device_error(void* stream, uint32_t* flags) {
     return MOE_ERR_HIP;
   if (flags) *flags = v;
   if (v == 0) return MOE_OK;
+  if (v & MOE_DEVERR_SYNC_TIMEOUT) static_scratch_invalidate();
   const uint32_t zero = 0;
   if (hipMemcpyToSymbol(HIP_SYMBOL(g_moe_device_error), &zero, sizeof zero, 0, hipMemcpyHostToDevice) != hipSuccess)
     return MOE_ERR_HIP;
