@@ -27,15 +27,18 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build(force: bool = False, out: Optional[str] = None, extra_flags=()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction) into `out` (the
+    in-tree liboracle.so by default); extra_flags are added to the command (e.g. a
+    host sanitizer)."""
+    target = out or _LIB
+    if force or out or not os.path.exists(target) or os.path.getmtime(target) < os.path.getmtime(_SRC):
+        tmp = target + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-D_GNU_SOURCE", "-o", tmp, _SRC, "-lm"]
+               "-fno-fast-math", "-D_GNU_SOURCE"] + list(extra_flags) + ["-o", tmp, _SRC, "-lm"]
         subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, target)
+    return target
 
 
 class _Mat(C.Structure):
@@ -55,7 +58,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        _lib = C.CDLL(build())
+        # QMOE_ORACLE_LIB names another build of the same source (e.g. a sanitizer build)
+        _lib = C.CDLL(os.environ.get("QMOE_ORACLE_LIB") or build())
         P = C.POINTER
         d = P(C.c_double)
         _lib.oracle_code.restype = C.c_int

@@ -25,7 +25,9 @@ __all__ = [
     "MOE_ERR_DEVICE_CHECK", "MOE_F32", "MOE_BF16", "MOE_DEVERR_BAD_SLOT",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so")
+# the in-tree build; QMOE_LIB names another build of the same sources instead (a sanitizer
+# build of the host code, or a variant to compare against)
+LIB_PATH = os.environ.get("QMOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED_SHAPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE_CHECK = \
     0, -1, -2, -3, -4, -5
