@@ -192,6 +192,57 @@ def flagged_rows(logits, k, gap=1e-4):
     return int(((srt[:, k - 1] - srt[:, k]) < gap).sum())
 
 
+TIMELINE_SLOTS = {  # slot -> meaning, per item kind of the whole-block decode kernel
+    "router": {0: "start", 1: "weights and x in", 2: "logits published"},
+    "shared gate/up": {0: "start", 1: "router published", 3: "dot products done", 4: "h stored"},
+    "routed gate/up": {0: "start", 1: "key words held", 2: "picks ranked", 3: "dot products done", 4: "h stored"},
+    "routed down": {0: "start", 1: "key words held", 2: "picks ranked", 3: "first h in", 4: "all h in",
+                    5: "dot products done", 7: "outputs stored"},
+    "shared down": {0: "start", 4: "all h in", 5: "dot products done", 7: "outputs stored"},
+    "combine": {0: "start", 1: "key words held", 2: "picks ranked", 4: "all shared h in", 5: "dot products done",
+                6: "all expert outputs in", 7: "y stored"},
+}
+
+
+def decode_timeline(q, shape, run_step, n_steps, dev):
+    """Per-phase times of the whole-block decode kernel from the timeline build's
+    per-workgroup stamps (100 MHz counter): for each item kind and phase, the median
+    and the slowest workgroup, in us from the earliest start of the step; medians of
+    those over n_steps steps."""
+    import ctypes as C
+    import numpy as np
+    import torch
+    E, k, d, f, fs = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff, shape.d_ff_shared
+    n = {"router": E // 2, "shared gate/up": fs // 16, "routed gate/up": k * (f // 16), "routed down": k * (d // 64),
+         "shared down": d // 64, "combine": d // 64}
+    grid = sum(n.values()) + 1
+    buf = torch.zeros(grid * 8, dtype=torch.int64, device=dev)
+    fn = q.lib().moe_debug_set_timeline
+    fn.restype, fn.argtypes = C.c_int, [C.c_void_p]
+    assert fn(buf.data_ptr()) == 0
+    per = {kind: {slot: [] for slot in slots} for kind, slots in TIMELINE_SLOTS.items()}
+    for i in range(n_steps):
+        buf.zero_()
+        run_step(i)
+        torch.cuda.synchronize()
+        t = buf.cpu().numpy().reshape(grid, 8).astype(np.float64)
+        t0 = t[:grid - 1, 0].min()
+        b = 0
+        for kind, cnt in n.items():
+            for slot in TIMELINE_SLOTS[kind]:
+                v = (t[b:b + cnt, slot] - t0) / 100.0  # 100 MHz ticks -> us
+                per[kind][slot].append((float(np.median(v)), float(v.max())))
+            b += cnt
+    assert fn(None) == 0
+    out = {}
+    for kind, slots in TIMELINE_SLOTS.items():
+        out[kind] = {"items": n[kind]}
+        for slot, name in slots.items():
+            a = np.asarray(per[kind][slot])
+            out[kind][name] = {"median_us": float(np.median(a[:, 0])), "slowest_us": float(np.median(a[:, 1]))}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +262,9 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the streaming-read and bf16 GEMM ceilings")
+    ap.add_argument("--timeline", type=int, default=0, metavar="STEPS",
+                    help="also record the decode kernel's per-phase timeline over STEPS eager steps (needs the "
+                         "timeline build: QMOE_LIB=.../libqmoe_timeline.so, from build.py --timeline)")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="rows in the oracle's timed CPU sample")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (counter calibration) and exit")
@@ -297,6 +351,16 @@ def main():
             "on active bytes (%.1f%% of 8 TB/s), %d flagged rows of %d"
             % (dec_steps, dec_ms * 1e3, dec_spread["median_us"], dec_spread["p10_us"], dec_spread["p90_us"], replays,
                dec_tok_s, dec_bw / 1e12, 100 * dec_bw / HBM_PEAK, dec_flagged, steps_per_graph))
+
+    timeline = None
+    if args.timeline > 0:
+        timeline = decode_timeline(q, shape, decode_step, args.timeline, dev)
+        log("decode timeline (us from the first workgroup's start; median workgroup / slowest workgroup, "
+            "medians over %d steps):" % args.timeline)
+        for kind, rec in timeline.items():
+            log("  %-15s (%3d items) " % (kind, rec["items"]) + "; ".join(
+                "%s %.2f / %.2f" % (name, v["median_us"], v["slowest_us"]) for name, v in rec.items()
+                if name != "items"))
 
     # ---------------------------------------------------------------- prefill
     def measure_prefill(R):
@@ -658,6 +722,8 @@ def main():
     }
     if sweep is not None:
         out["prefill_chunk_sweep"] = sweep
+    if timeline is not None:
+        out["decode_timeline"] = timeline
     if cache is not None:
         out["tiered_residency"] = cache
     print(json.dumps(out), flush=True)

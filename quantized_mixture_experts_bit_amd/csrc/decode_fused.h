@@ -2,9 +2,10 @@
 //
 // The dependency chain for one token is router -> top-k -> routed gate/up ->
 // GeGLU -> routed down -> combine. The shared expert does not depend on the
-// routing and streams from the start (the pages run the shared-expert branch
-// while the routed experts are being fetched: blog-mushroom article
-// "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook", section "Why 26B Fits in 2 GB").
+// routing and streams while the routed experts are picked and fetched (the pages
+// run the shared-expert branch while the routed experts are being read in:
+// blog-mushroom article "TurboFieldfare: Gemma 4 26B on an 8 GB MacBook", section
+// "Why 26B Fits in 2 GB"); its weight loads start once the router has published.
 //
 // Work items, one workgroup each, in dependency order (an item waits only for
 // items before it; the launch is used only when the whole grid is resident),
@@ -103,6 +104,24 @@ struct FusedSmem {
   int sel_e[17];
   float selw[16];
 };
+
+// Timeline build (QMOE_TIMELINE): thread 0 of each workgroup stamps the 100 MHz
+// real-time counter at the phase boundaries of its item into g_timeline[block][slot]
+// (kStamps slots per block; the slot meanings per item kind are listed at each
+// QMOE_STAMP). The default build compiles the stamps away.
+constexpr int kStamps = 8;
+#ifdef QMOE_TIMELINE
+__device__ uint64_t* g_timeline = nullptr;
+#define QMOE_STAMP(slot)                                                                        \
+  do {                                                                                          \
+    if (threadIdx.x == 0 && g_timeline)                                                         \
+      g_timeline[(size_t)blockIdx.x * kStamps + (slot)] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+#else
+#define QMOE_STAMP(slot) \
+  do {                   \
+  } while (0)
+#endif
 
 __device__ __forceinline__ uint32_t ld_agent_u(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -278,6 +297,7 @@ __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, Fu
   const uint64_t* lk = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride + kLgKeys;
   poll_tagged<1>([&](int i) { return lk + i; }, E, tag, [&](int i, uint32_t p) { S.kp[i] = p; });
   __syncthreads();
+  QMOE_STAMP(1);  // routed gate/up, down, combine: every key word held
   const int idbits = E <= 128 ? 7 : 8;
   // thread t: expert t % E against the competitors of share t / E (256 / E shares of
   // 64, 64 or 16 keys, all of a 32-key run read before the first comparison)
@@ -313,6 +333,7 @@ __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, Fu
     load_logits(F, tag, S);
     rank_topk(S.key, E, k, S.rank, S.sel_e);
   }
+  QMOE_STAMP(2);  // routed gate/up, down, combine: picks ranked
 }
 
 // The blob of the expert picked for `slot` (nullptr and the error flag if its table
@@ -359,6 +380,7 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
   }
   if (tid == 0) arrive_epoch(F, epoch);  // before the first wait, which covers it
   stage_x<XT, true>(x, F.d, S);
+  QMOE_STAMP(1);  // router: weights and x in
   double acc = 0.0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
@@ -407,6 +429,7 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
       put_tag(dst + kLgKeys + e, ((uint32_t)(key >> (33 + idbits)) << idbits) | (uint32_t)(F.E - 1 - e), tag);
     }
   }
+  QMOE_STAMP(2);  // router: logits and keys published
 }
 
 // ------------------------------------------------------------------ gate/up item
@@ -469,6 +492,12 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
   // the shared expert's weights stream from the start; a routed expert's once it is known
   const uint8_t* blob = F.shared_blob;
   if (!routed) {
+    // the shared expert's weights start streaming once the router items have published
+    // their keys: the router's own loads, which head the chain, then meet an idle
+    // memory system instead of the shared expert's 10 MB
+    const uint64_t* lk = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride + kLgKeys;
+    poll_tagged<1>([&](int i) { return lk + i; }, F.E, tag, [&](int i, uint32_t p) { S.kp[i] = p; });
+    QMOE_STAMP(1);  // shared gate/up: the router has published
     load(blob);
     if (tid == 0) arrive_epoch(F, epoch);
   }
@@ -499,6 +528,7 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
       }
     }
   }
+  QMOE_STAMP(3);  // gate/up: dot products done
   S.red[0][wave][lane] = acc[0];
   S.red[1][wave][lane] = acc[1];
   __syncthreads();
@@ -516,6 +546,7 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
     put_tag(&F.h_tag[copy * F.h_stride + (size_t)slot * F.fmax + nb * 64 + q4 * kFusedRows + r],
             __float_as_uint(gelu_tanh(v[0]) * v[1]), tag);
   }
+  QMOE_STAMP(4);  // gate/up: h stored
 }
 
 // ------------------------------------------------------------------ down item (+ combine)
@@ -648,6 +679,7 @@ __device__ __forceinline__ void fused_combine(const FusedArgs& F, int ob, float 
   poll_tagged<5>([&](int i) { return F.eo_tag + (size_t)(i >> 6) * F.d + ob * 64 + (i & 63); }, 64 * (k + 1), tag,
                  [&](int i, uint32_t p) { S.eo[i >> 6][i & 63] = __uint_as_float(p); });
   __syncthreads();
+  QMOE_STAMP(6);  // combine: every expert output in
   if (tid < 64) {
     float yv = r + S.eo[k][lane];
     for (int s = 0; s < k; ++s) yv = fmaf(S.selw[s], S.eo[s][lane], yv);
@@ -692,6 +724,7 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
     // the rest of h is produced
     if (tid == 0) arrive_epoch(F, epoch);
     sc = gather_h<true>(hsrc, g0 * kGroup, g1 * kGroup, tag, S, [&] {
+      QMOE_STAMP(3);  // routed down: the first values of h in
       if (rowblock) w.load(rowblock, g0, g1, wave, lane);
     });
   } else {
@@ -700,8 +733,10 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
     if (kind == 2) pick_weights(F, tag, S);  // the logits are out long before the shared h
     sc = gather_h(hsrc, g0 * kGroup, g1 * kGroup, tag, S);
   }
+  QMOE_STAMP(4);  // down, combine: all of h in
   const float acc = rowblock ? w.dot_lds(g0, g1, wave, S.xb, S.hsum) : 0.0f;
   const float r = reduce_waves4(acc, S.red[0], wave, lane) * (1.0f / sc);  // exact: sc is a power of two
+  QMOE_STAMP(5);  // down, combine: dot products done
   if (kind == 2) {
     fused_combine(F, ob, r, tag, S);
   } else if (wave == 0) {
@@ -709,6 +744,7 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
     if (kind == 0) F.expert_out[(size_t)slot * F.d + n] = r;
     put_tag(&F.eo_tag[(size_t)slot * F.d + n], __float_as_uint(r), tag);
   }
+  QMOE_STAMP(7);  // down: outputs stored; combine: y stored
 }
 
 // ------------------------------------------------------------------ the kernel
@@ -720,6 +756,7 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
 template <typename XT>
 __global__ __launch_bounds__(256, 4) void k_decode_fused(FusedArgs F, const XT* __restrict__ x) {
   __shared__ FusedSmem S;
+  QMOE_STAMP(0);  // every item: started
   const uint32_t epoch = read_epoch(F);
   const uint32_t tag = epoch + 1u;
   if (blockIdx.x == gridDim.x - 1) return epoch_keeper(F, epoch);

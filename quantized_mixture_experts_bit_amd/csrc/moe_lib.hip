@@ -74,7 +74,7 @@ size_t fused_h_stride(const moe_shape* s) {
 struct Ws {
   size_t gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, router_partial, gu_partial, h_hi,
       h_lo, h_gsum,
-      shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, total;
+      shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, pf_xg, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -107,6 +107,7 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.pf_hmaxp = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
   w.pf_Hh = take(sizeof(uint16_t) * R * ((size_t)k * s->d_ff + s->d_ff_shared));
   w.pf_hsc = take(sizeof(float) * R * (k + 1));
+  w.pf_xg = take(sizeof(float) * R * ((d / 64 + 3) & ~3));  // rows padded to a multiple of 4 groups
   w.total = o;
   return w;
 }
@@ -147,10 +148,10 @@ moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ER
 
 template <typename XT>
 void launch_router(const moe_shape* s, const moe_layer* L, const XT* x, int rows, const float* off, int32_t* idx,
-                   float* w, double* logits, void* ws, const Ws& W, hipStream_t st) {
+                   float* w, double* logits, void* ws, const Ws& W, hipStream_t st, float* xg = nullptr) {
   double* part = at<double>(ws, W.router_partial);
   const int blocks = cdiv(rows, 16) * (s->n_experts / 16) * kRouterSplits;
-  k_router_logits<XT><<<blocks, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, part);
+  k_router_logits<XT><<<blocks, 256, 0, st>>>(L->router_blob, x, rows, s->d_model, s->n_experts, part, xg);
   k_router_select<<<rows, 256, 0, st>>>(part, rows, s->n_experts, s->top_k, off, idx, w, logits);
 }
 
@@ -293,6 +294,7 @@ PrefillArgs prefill_args(const moe_shape* s, const moe_layer* L, int rows, const
   A.hmaxp = at<float>(ws, W.pf_hmaxp);
   A.Hh = at<uint16_t>(ws, W.pf_Hh);
   A.hsc = at<float>(ws, W.pf_hsc);
+  A.xg = at<float>(ws, W.pf_xg);
   return A;
 }
 
@@ -320,12 +322,15 @@ int persistent_grid(int resident, int items) {
 }
 
 // one gate/up launch, the H conversion and one down launch covering the routed
-// tiles and/or the shared expert's tiles
+// tiles and/or the shared expert's tiles; with group_sums, first the activations'
+// group sums (when the router kernel has not left them)
 template <typename XT>
-void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, hipStream_t st) {
+void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, bool group_sums, hipStream_t st) {
   static int cap_gu[64], cap_dn[64];
   if (!routed) A.routed_mtiles = 0;
   if (!shared) A.shared_mtiles = 0;
+  if (group_sums)
+    k_group_sums<XT><<<cdiv(A.rows, 16) * kRouterSplits, 256, 0, st>>>(x, A.rows, A.d, const_cast<float*>(A.xg));
   // items at most (routed tile count bounded by the pair count plus one per expert)
   const int gu_items = xcd_blocks(A.routed_mtiles, A.f / 64) + xcd_blocks(A.shared_mtiles, A.fs / 64);
   if (gu_items == 0) return;
@@ -514,9 +519,9 @@ moe_status moe_expert_ffn_prefill_chunk(const moe_shape* s, const moe_layer* L, 
   PrefillArgs A = prefill_args(s, L, rows, offset, perm, expert_out, ws);
   hipStream_t hs = (hipStream_t)stream;
   if (dt == MOE_BF16)
-    launch_prefill(A, (const uint16_t*)x, true, false, hs);
+    launch_prefill(A, (const uint16_t*)x, true, false, true, hs);
   else
-    launch_prefill(A, (const float*)x, true, false, hs);
+    launch_prefill(A, (const float*)x, true, false, true, hs);
   return launched();
 }
 
@@ -543,9 +548,9 @@ moe_status moe_combine(const moe_shape* s, const moe_layer* L, const void* x, mo
   }
   PrefillArgs A = prefill_args(s, L, rows, nullptr, nullptr, nullptr, ws);
   if (dt == MOE_BF16)
-    launch_prefill(A, (const uint16_t*)x, false, true, hs);
+    launch_prefill(A, (const uint16_t*)x, false, true, true, hs);
   else
-    launch_prefill(A, (const float*)x, false, true, hs);
+    launch_prefill(A, (const float*)x, false, true, true, hs);
   k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, topk_w, rows,
                                                                  s->d_model, s->top_k, y, residual);
   return launched();
@@ -590,17 +595,19 @@ moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void*
   if (!idx || !w || !count || !offset || !perm || !inv_perm || !expert_out || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(expert_out) || !aligned16(y) || ((uintptr_t)residual & 7u)) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
+  const Ws W = ws_layout(s, rows);
+  float* xg = at<float>(ws, W.pf_xg);  // the router kernel leaves the group sums for gate/up
   if (dt == MOE_BF16)
-    launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, nullptr, ws, ws_layout(s, rows), hs);
+    launch_router(s, L, (const uint16_t*)x, rows, off, idx, w, nullptr, ws, W, hs, xg);
   else
-    launch_router(s, L, (const float*)x, rows, off, idx, w, nullptr, ws, ws_layout(s, rows), hs);
+    launch_router(s, L, (const float*)x, rows, off, idx, w, nullptr, ws, W, hs, xg);
   const size_t lds = sizeof(int32_t) * kGroupWaves * s->n_experts;
   k_group<<<1, 1024, lds, hs>>>(idx, rows * s->top_k, s->n_experts, count, offset, perm, inv_perm);
   PrefillArgs A = prefill_args(s, L, rows, offset, perm, expert_out, ws);
   if (dt == MOE_BF16)
-    launch_prefill(A, (const uint16_t*)x, true, true, hs);
+    launch_prefill(A, (const uint16_t*)x, true, true, false, hs);
   else
-    launch_prefill(A, (const float*)x, true, true, hs);
+    launch_prefill(A, (const float*)x, true, true, false, hs);
   k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, w, rows,
                                                                  s->d_model, s->top_k, y, residual);
   return launched();
@@ -617,6 +624,16 @@ const char* moe_status_string(moe_status st) {
   }
   return "unknown status";
 }
+
+#ifdef QMOE_TIMELINE
+// Timeline build only: device buffer of [grid][kStamps] uint64 that k_decode_fused fills
+// with per-workgroup phase stamps (NULL switches the stamps off).
+moe_status moe_debug_set_timeline(void* buf) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &buf, sizeof buf, 0, hipMemcpyHostToDevice) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+#endif
 
 moe_status moe_check_device_error(void* stream, uint32_t* flags) {
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;

@@ -10,9 +10,11 @@
 // The 4-bit weights are not dequantised element by element. The affine form is
 // factored out of the contraction per group of 64 columns:
 //   sum_i (s q_i + b) a_i = s * sum_i c_i a_i + (b - s c0) * A_g,   c_i = c0 + q_i,
-// where A_g is the group sum of the activations. MFMA computes sum_i c_i a_i and
-// A_g (a product with a column of ones) per group from the very operands it
-// multiplies; the epilogue applies s and b. Codes and activations enter exactly:
+// where A_g is the group sum of the activations. MFMA computes sum_i c_i a_i per
+// group; the epilogue applies s and b. A_g of the gate/up activations is computed
+// once per chunk (by the router kernel, or k_group_sums for the split calls) and
+// held in LDS per tile; A_g of H comes from the threads that stage each H group.
+// Codes and activations enter exactly:
 //   gate/up: x is bf16 (exact; fp32 x is split into two bf16 terms hi + lo),
 //            c_i = 128 + q_i as bf16 from one mask-and-or per code pair (c0 = 128);
 //   down:    H rows scaled so their largest |h| lands in [2^14, 2^15) and rounded
@@ -35,6 +37,8 @@ namespace qmoe {
 constexpr int kLdsStride = 72;  // halfs per LDS row: 64 + 8 padding (144 B) against bank conflicts
 constexpr int kRing = 4;        // weight groups in flight per wavefront
 constexpr int kXcds = 8;        // accelerator dies, each with its own L2
+constexpr int kMaxG = 96;       // groups of the reduction: d_model <= 6144
+
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -62,6 +66,7 @@ struct PrefillArgs {
   int d, f, fs, n_experts, top_k, rows;
   int routed_mtiles;      // upper bound of routed 64-row tiles
   int shared_mtiles;      // 64-row tiles of the shared expert
+  const float* xg;        // group sums of the activations, fp32 [rows][d/64] (the router kernel's)
   float* H;               // routed GeGLU output, fp32 [rows*top_k][f] (sorted-pair order)
   float* Hs;              // shared GeGLU output, fp32 [rows][fs]
   float* hmaxp;           // max |h| per (row, 64-column block): routed [rows*top_k][f/64], then shared [rows][fs/64]
@@ -230,25 +235,36 @@ __device__ __forceinline__ void zero_acc(f32x4_t& a) { a = f32x4_t{0.f, 0.f, 0.f
 
 // ---------------------------------------------------------------- gate/up + GeGLU
 
-// LDS of the gate/up kernel: double-buffered activation tiles (bf16 hi, and lo for
-// fp32 x) and the per-wave row maxima of |h|
+// LDS of the gate/up kernel: double-buffered activation stages of up to two groups
+// (bf16 hi, and lo for fp32 x, whose stages hold one group), the group sums of the
+// tile's rows (group-major: xgL[g][row]) and the per-wave row maxima of |h|
 template <bool LO>
 struct GateupSmem {
-  __attribute__((aligned(16))) uint16_t Xs[2][64 * kLdsStride];
-  __attribute__((aligned(16))) uint16_t Xls[LO ? 2 : 1][LO ? 64 * kLdsStride : 8];
+  static constexpr int kMaxStage = LO ? 1 : 2;  // groups per stage
+  __attribute__((aligned(16))) uint16_t Xs[2 * 64 * (kMaxStage * 64 + 8)];
+  __attribute__((aligned(16))) uint16_t Xls[LO ? 2 * 64 * 72 : 8];
+  __attribute__((aligned(16))) float xgL[kMaxG * 64];
   float hmL[4][64];
 };
 
 // One work item = (64-row tile, 64 d_ff columns). Wave w owns d_ff columns [16w, +16)
 // of both gate and up (so GeGLU runs in registers) for every row of the tile.
-template <typename XT>
+// Activations are staged SG groups at a time (one barrier per stage); within a stage
+// the K groups need no barrier between them, so the scheduler can overlap one group's
+// epilogue with the next group's matrix work. The group sums X_g of the bias term come
+// from LDS (filled once per tile from the chunk's precomputed sums), not from MFMAs.
+template <typename XT, int SG>
 __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __restrict__ x, const MTile& T, int fc,
                                             bool shared, GateupSmem<sizeof(XT) == 4>& S) {
   constexpr bool LO = sizeof(XT) == 4;  // fp32 x: hi + lo bf16 terms
-  constexpr int RA = LO ? 2 : 4;        // activation groups in flight
+  static_assert(!LO || SG == 1, "fp32 activations stage one group at a time");
+  static_assert(kRing % SG == 0 && (kRing / SG) % 2 == 0, "stages alternate buffers within the ring");
+  constexpr int RA = LO ? 2 : 4;        // activation groups in flight (a multiple of SG)
   constexpr int NV = LO ? 4 : 2;        // 16-byte loads per thread per group
-  auto& Xs = S.Xs;
-  auto& Xls = S.Xls;
+  constexpr int kStride = SG * 64 + 8;  // halfs per staged row: SG groups + 8 padding against bank conflicts
+  constexpr int kBuf = 64 * kStride;
+  uint16_t* Xs = S.Xs;
+  uint16_t* Xls = S.Xls;
   auto& hmL = S.hmL;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -265,7 +281,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   BRing<2> B;
   B.init(wrow, lane);
 
-  // activation staging: thread -> tile row tid/4, 16 values at column (tid%4)*16.
+  // activation staging: thread -> tile row tid/4, 16 values at column (tid%4)*16 of a group.
   // Rows past the tile's end repeat its first row: MFMA output rows depend on their
   // own A rows only, and those rows are never stored, so the loads need no branch.
   const int xr = tid >> 2, xq = tid & 3;
@@ -279,9 +295,11 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
 #pragma unroll
     for (int v = 0; v < NV; ++v) xa[slot][v] = bld16(xres, xvo + 16 * v, (uint32_t)(g * kGroup * sizeof(XT)));
   };
+  // ring slot -> its place in a stage buffer (group g sits in slot g % RA, place g % SG)
   auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&Xs[buf][xr * kLdsStride + xq * 16]);
+    constexpr int pos = slot % SG;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&Xs[buf * kBuf + xr * kStride + pos * 64 + xq * 16]);
     if (!LO) {
       dst[0] = xa[slot][0];
       dst[1] = xa[slot][1];
@@ -306,7 +324,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
           lo[2 * v + p] = l2;
         }
       }
-      u32x4_t* dl = reinterpret_cast<u32x4_t*>(&Xls[buf][xr * kLdsStride + xq * 16]);
+      u32x4_t* dl = reinterpret_cast<u32x4_t*>(&Xls[buf * kBuf + xr * kStride + pos * 64 + xq * 16]);
       dst[0] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
       dst[1] = u32x4_t{hi[4], hi[5], hi[6], hi[7]};
       dl[0] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
@@ -314,17 +332,48 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
     }
   };
   // prologue: the loads in the order the steady state issues them (weights of group
-  // j, then activations of group j + 1), so the wait counts agree on entry
+  // j, then activations of group j + 1), so the wait counts agree on entry; then the
+  // first stage into buffer 0 and its ring slots refilled
   aload(ic<0>{}, 0);
   static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     B.load(jc, wres, min(j, G - 1));
     if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(j + 1, G - 1));
     if constexpr (j + 1 == RA) {
-      astore(ic<0>{}, 0);
-      aload(ic<0>{}, min(RA, G - 1));
+      static_for<SG>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value;
+        astore(ic<p>{}, 0);
+        aload(ic<p>{}, min(RA + p, G - 1));
+      });
     }
   });
+  // the group sums of the tile's rows into LDS, group-major (rows past the tile's end
+  // take row 0's, as the activations do): thread t loads row t%64, groups 4 (t/64 + 4u)
+  // .. +3 as one 16-byte load (rows of xg are padded to a multiple of four groups; a
+  // load past the array returns zeros), all loads issued before the first store
+  {
+    const int r = tid & 63;
+    const int src = r < T.mrows ? r : 0;
+    const int Gp = (G + 3) & ~3;
+    const int srow = T.e >= 0 ? A.perm[T.m0 + src] / A.top_k : T.m0 + src;
+    const rsrc_t gres = buf_rsrc(A.xg, (uint32_t)((size_t)A.rows * Gp * 4));
+    constexpr int kQ = 3;  // quads of groups per thread per batch: 48 groups (d_model 3072) in one batch
+    for (int u0 = 0; 16 * u0 < G; u0 += kQ) {
+      u32x4_t v[kQ];
+#pragma unroll
+      for (int u = 0; u < kQ; ++u)
+        v[u] = bld16(gres, (uint32_t)((srow * Gp + 4 * ((tid >> 6) + 4 * (u0 + u))) * 4), 0);
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) {
+        const int g = 4 * ((tid >> 6) + 4 * (u0 + u));
+        if (g < G) {  // wave-uniform
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (g + c < G) S.xgL[(g + c) * 64 + r] = __uint_as_float(v[u][c]);
+        }
+      }
+    }
+  }
   __syncthreads();
 
   // The compute is compiled for NMB = 1, 2 and 4 blocks of 16 rows (3 runs as 4), so
@@ -338,42 +387,44 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
       zero_acc(acc[mb][0]);
       zero_acc(acc[mb][1]);
     }
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    // One K group: MFMAs from LDS buffer j&1 and weight slot j; then the weight
-    // slot is refilled with group g + kRing and the activation slot staged next is
-    // refilled with group g + 1 + RA, both clamped to the last group (the surplus
-    // loads near the end are never used). The steady-state loop is
-    // straight-line code over kRing groups, so every ring slot keeps its own
-    // registers and no wait covers a load younger than the one it needs.
+    // One stage = SG K groups from LDS buffer (j0 / SG) & 1 and weight slots j0.. j0 + SG - 1:
+    // per group the codes of its slot become MFMA operands and the slot is refilled with
+    // group g + kRing; after the stage's MFMAs the next stage is staged into the other
+    // buffer from the activation ring and its slots refilled SG stages ahead (loads past
+    // the last group are clamped to it and never used). The steady-state loop is
+    // straight-line code over kRing groups, so every ring slot keeps its own registers
+    // and no wait covers a load younger than the one it needs.
     const NibK nk;
-    auto step = [&](auto jc, int g) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int buf = j & 1;
-      bf16x8_t bfr[2][2];
-      float s[2], bb[2];
+    auto stage = [&](auto jc, int g) __attribute__((always_inline)) {
+      constexpr int j0 = decltype(jc)::value;
+      constexpr int buf = (j0 / SG) & 1;
+      static_for<SG>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int j = j0 + p;
+        bf16x8_t bfr[2][2];
+        float s[2], bb[2];
   #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        bfr[m][0] = codes_bf16(B.cw[j][m][0], nk);
-        bfr[m][1] = codes_bf16(B.cw[j][m][1], nk);
-        s[m] = bf16_lo(B.sb[j][m]);
-        bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
-      }
-      B.load(jc, wres, min(g + kRing, G - 1));
+        for (int m = 0; m < 2; ++m) {
+          bfr[m][0] = codes_bf16(B.cw[j][m][0], nk);
+          bfr[m][1] = codes_bf16(B.cw[j][m][1], nk);
+          s[m] = bf16_lo(B.sb[j][m]);
+          bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
+        }
+        B.load(ic<j>{}, wres, min(g + p + kRing, G - 1));
   #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        {
-          const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
-          const bf16x8_t a0 = lds_frag<bf16x8_t>(&Xs[buf][ao]);
-          const bf16x8_t a1 = lds_frag<bf16x8_t>(&Xs[buf][ao + 32]);
-          f32x4_t ag = mfma(a1, ones, mfma(a0, ones, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int ao = buf * kBuf + (16 * mb + (lane & 15)) * kStride + p * 64 + 8 * (lane >> 4);
+          const bf16x8_t a0 = lds_frag<bf16x8_t>(&Xs[ao]);
+          const bf16x8_t a1 = lds_frag<bf16x8_t>(&Xs[ao + 32]);
+          // group sums of rows 16 mb + 4 (lane / 16) + i, the rows of this lane's outputs
+          const f32x4_t ag = *reinterpret_cast<const f32x4_t*>(&S.xgL[(g + p) * 64 + 16 * mb + 4 * (lane >> 4)]);
           f32x4_t t[2];
   #pragma unroll
           for (int m = 0; m < 2; ++m) t[m] = mfma(a1, bfr[m][1], mfma(a0, bfr[m][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
           if (LO) {
-            const bf16x8_t l0 = lds_frag<bf16x8_t>(&Xls[buf][ao]);
-            const bf16x8_t l1 = lds_frag<bf16x8_t>(&Xls[buf][ao + 32]);
-            ag = mfma(l1, ones, mfma(l0, ones, ag));
+            const bf16x8_t l0 = lds_frag<bf16x8_t>(&Xls[ao]);
+            const bf16x8_t l1 = lds_frag<bf16x8_t>(&Xls[ao + 32]);
   #pragma unroll
             for (int m = 0; m < 2; ++m) t[m] = mfma(l1, bfr[m][1], mfma(l0, bfr[m][0], t[m]));
           }
@@ -382,23 +433,28 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[m][i], fmaf(bb[m], ag[i], acc[mb][m][i]));
         }
-      }
-      // next activation group into the other buffer (its readers passed the last barrier)
-      astore(ic<(j + 1) % RA>{}, buf ^ 1);
-      aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, G - 1));
+      });
+      // the next stage into the other buffer (its readers passed the last barrier)
+      static_for<SG>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int slot = (j0 + SG + p) % RA;
+        astore(ic<slot>{}, buf ^ 1);
+        aload(ic<slot>{}, min(g + SG + p + RA, G - 1));
+      });
       __syncthreads();
     };
     int g0 = 0;
-    for (; g0 + kRing <= G; g0 += kRing) {
-      step(ic<0>{}, g0);
-      step(ic<1>{}, g0 + 1);
-      step(ic<2>{}, g0 + 2);
-      step(ic<3>{}, g0 + 3);
-    }
-    // the last G % kRing groups
-    if (g0 < G) step(ic<0>{}, g0);
-    if (g0 + 1 < G) step(ic<1>{}, g0 + 1);
-    if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
+    for (; g0 + kRing <= G; g0 += kRing)
+      static_for<kRing / SG>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int st = decltype(sc)::value;
+        stage(ic<st * SG>{}, g0 + st * SG);
+      });
+    // the last G % kRing groups (a multiple of SG)
+    static_for<kRing / SG - 1>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int st = decltype(sc)::value;
+      if (g0 + st * SG < G) stage(ic<st * SG>{}, g0 + st * SG);
+    });
+
 
     // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16
     float* H = shared ? A.Hs : A.H;
@@ -454,7 +510,11 @@ __global__ __launch_bounds__(256, 2) void k_prefill_gateup(PrefillArgs A, const 
       xcd_item(item - ns, nrt, ncr, mt, fc);
       if (mt >= nrt || !tile_at(A, M, mt, T)) continue;
     }
-    gateup_tile<XT>(A, x, T, fc, shared, S);
+    // bf16 activations with an even group count stage two groups per barrier
+    if (sizeof(XT) == 2 && (A.d / kGroup) % 2 == 0)
+      gateup_tile<XT, sizeof(XT) == 2 ? 2 : 1>(A, x, T, fc, shared, S);
+    else
+      gateup_tile<XT, 1>(A, x, T, fc, shared, S);
     __syncthreads();  // the next item reuses the LDS
   }
 }

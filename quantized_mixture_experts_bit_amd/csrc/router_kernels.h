@@ -103,6 +103,16 @@ struct XRow16<uint16_t> {
     const uint32_t w = u4_at(v[t >> 3], (t >> 1) & 3);
     return (double)((t & 1) ? bf16_hi(w) : bf16_lo(w));
   }
+  // the 16 values added in order in fp32
+  __device__ __forceinline__ float sum16() const {
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t w = u4_at(v[t >> 3], (t >> 1) & 3);
+      s += (t & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+    return s;
+  }
 };
 template <>
 struct XRow16<float> {
@@ -112,7 +122,34 @@ struct XRow16<float> {
     for (int c = 0; c < 4; ++c) v[c] = ldg16(reinterpret_cast<const uint8_t*>(p) + 16 * c);
   }
   __device__ __forceinline__ double at(int t) const { return (double)__uint_as_float(u4_at(v[t >> 2], t & 3)); }
+  __device__ __forceinline__ float sum16() const {
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) s += __uint_as_float(u4_at(v[t >> 2], t & 3));
+    return s;
+  }
 };
+
+// Group sums X_g[row][g] = sum of the 64 activations of group g of the row, in fp32:
+// the four lanes (i, j) holding 16 values each add theirs in order, then the quarter
+// sums are added as (q0 + q1) + (q2 + q3). Used by the prefill gate/up kernel for the
+// bias term of its affine epilogue. Wavefront `part` of the router mapping holds the
+// groups part + kRouterParts n; lane i + 16 j holds row i, quarter j.
+template <typename XT>
+__device__ __forceinline__ void store_group_sums(const XRow16<XT>* xv, int part, int G, int row, bool row_ok,
+                                                 float* __restrict__ xg) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int n = 0; n < kRouterMaxGPP; ++n) {
+    const int g = part + n * kRouterParts;
+    if (g < G) {  // wave-uniform
+      float q = xv[n].sum16();
+      q += __shfl_xor(q, 16, 64);
+      q += __shfl_xor(q, 32, 64);
+      if (lane < 16 && row_ok) xg[(size_t)row * ((G + 3) & ~3) + g] = q;  // rows padded to 4 groups
+    }
+  }
+}
 
 // Router logits over part of the reduction, on the fp64 matrix cores. Grid
 // ceil(rows/16) * (n_experts/16) * kRouterSplits workgroups of 256 threads; workgroup
@@ -128,7 +165,7 @@ struct XRow16<float> {
 template <typename XT>
 __global__ __launch_bounds__(256) void k_router_logits(const uint8_t* __restrict__ router, const XT* __restrict__ x,
                                                        int rows, int d, int n_experts,
-                                                       double* __restrict__ partial) {
+                                                       double* __restrict__ partial, float* __restrict__ xg) {
   __shared__ double red[4][256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,6 +195,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint8_t* __restrict
       xv[n].load(xr + g * kGroup);
     }
   }
+  // the workgroups of the first 16 experts also leave the rows' group sums (if asked)
+  if (xg && et == 0) store_group_sums<XT>(xv, part, G, rt * 16 + i, rt * 16 + i < rows, xg);
   f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int n = 0; n < kRouterMaxGPP; ++n) {
@@ -179,6 +218,28 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint8_t* __restrict
   if (orow < rows)
     partial[((size_t)split * rows + orow) * n_experts + et * 16 + (tid & 15)] =
         ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+// The group sums alone (the prefill calls that do not run the router): the router
+// kernel's mapping without the experts, so the sums are the same bits. Grid
+// ceil(rows/16) * kRouterSplits workgroups of 256 threads.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_group_sums(const XT* __restrict__ x, int rows, int d,
+                                                    float* __restrict__ xg) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x % kRouterSplits, rt = blockIdx.x / kRouterSplits;
+  const int G = d / kGroup, part = split * 4 + wave;
+  const int i = lane & 15, j = lane >> 4;
+  const int row = min(rt * 16 + i, rows - 1);
+  const XT* xr = x + (size_t)row * d + 16 * j;
+  XRow16<XT> xv[kRouterMaxGPP];
+#pragma unroll
+  for (int n = 0; n < kRouterMaxGPP; ++n) {
+    const int g = part + n * kRouterParts;
+    if (g < G) xv[n].load(xr + g * kGroup);
+  }
+  store_group_sums<XT>(xv, part, G, rt * 16 + i, rt * 16 + i < rows, xg);
 }
 
 // One workgroup (256 threads) per row: the row's logits are the kRouterSplits partial
