@@ -261,6 +261,32 @@ moe_status moe_layer_decode(const moe_shape* shape, const moe_layer* layer, cons
                             float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One decode row through n_layers stacked blocks (layers[l]: host array of each layer's
+ * weights, every layer of the same shape), with the residual add between them:
+ *   x_{l+1} = bf16_rne(fp32(x_l) + y_l),  y_l = the block of layer l on x_l.
+ * x is bf16 [d_model], in: x_0, out: x_{n_layers}. The pages run the 30 MoE layers of
+ * a token one after another (blog-mushroom article "TurboFieldfare: Gemma 4 26B on an
+ * 8 GB MacBook", section "Why 26B Fits in 2 GB"); their decode step spends a third of
+ * its time waiting between command buffers (same article, decode-step breakdown table
+ * in section 实测数据). Here the whole stack is one launch when the shape fits the
+ * whole-block decode kernel and n_layers <= 32: each workgroup keeps its item from layer
+ * to layer and streams the next layer's routing-independent weights while the previous
+ * layer finishes; otherwise the layers run one call each. Same results as n_layers calls
+ * of moe_layer_decode with residual_bf16 = x.
+ *   logit_offsets  host array [n_layers] of device [n_experts] offsets, or NULL (none)
+ *   topk_idx, topk_w  [n_layers][top_k];  expert_out [n_layers][top_k][d_model],
+ *   y [n_layers][d_model] fp32 and x_layers [n_layers][d_model] bf16 (each layer's input)
+ *   may be NULL. The workspace is moe_workspace_bytes(shape, 1), as for moe_layer_decode
+ *   (and shares its call counter).
+ * Errors: those of moe_layer_decode for x and every layer; MOE_ERR_INVALID_ARG for
+ * layers NULL, n_layers < 0, topk_idx or topk_w NULL, or a non-NULL expert_out, y or
+ * x_layers not 16-byte aligned. n_layers = 0 returns MOE_OK and launches nothing.
+ */
+moe_status moe_stack_decode(const moe_shape* shape, const moe_layer* layers, int32_t n_layers, uint16_t* x,
+                            const float* const* logit_offsets, int32_t* topk_idx, float* topk_w, float* expert_out,
+                            float* y, uint16_t* x_layers, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_layer_decode for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
  * workspace: its scratch is a static device array of the library (4 MiB per GPU the

@@ -18,7 +18,8 @@ __all__ = [
     "moe_expert_blob_bytes", "moe_shared_blob_bytes", "moe_router_blob_bytes",
     "moe_pack_matrix4", "moe_pack_matrix8", "moe_unpack_matrix4", "moe_unpack_matrix8",
     "moe_router_topk", "moe_group_by_expert", "moe_expert_ffn_decode", "moe_expert_ffn_prefill_chunk",
-    "moe_combine", "moe_layer_decode", "moe_layer_decode_noalloc", "moe_layer_prefill", "moe_status_string",
+    "moe_combine", "moe_layer_decode", "moe_layer_decode_noalloc", "moe_stack_decode", "moe_layer_prefill",
+    "moe_status_string",
     "moe_check_device_error",
     "moe_cache_create", "moe_cache_acquire", "moe_cache_stats", "moe_cache_destroy",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED_SHAPE", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
@@ -98,6 +99,7 @@ def lib() -> C.CDLL:
             "moe_combine": (st, [S, Ly, _P, st, i32, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
             "moe_layer_decode": (st, [S, Ly, _P, st, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
             "moe_layer_decode_noalloc": (st, [S, Ly, _P, st, _P, _P, _P, _P, _P, _P, _P]),
+            "moe_stack_decode": (st, [S, Ly, i32, _P, C.POINTER(_P), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
             "moe_layer_prefill": (st, [S, Ly, _P, st, i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        C.c_size_t, _P]),
             "moe_status_string": (C.c_char_p, [st]),
@@ -255,6 +257,20 @@ def moe_layer_decode_noalloc(shape, layer: moe_layer, x, logit_offset, topk_idx,
     _check(lib().moe_layer_decode_noalloc(C.byref(as_shape(shape)), C.byref(layer), _dptr(x), _dtype_code(x),
                                           _dptr(logit_offset), _dptr(topk_idx), _dptr(topk_w), _dptr(expert_out),
                                           _dptr(y), _dptr(residual), _stream(stream)), "moe_layer_decode_noalloc")
+
+
+def moe_stack_decode(shape, layers, x, logit_offsets, topk_idx, topk_w, expert_out, y, x_layers, ws,
+                     stream=None) -> None:
+    """One bf16 row x through the layers (a sequence of moe_layer), residual in place.
+    logit_offsets: None or one device tensor (or None) per layer."""
+    n = len(layers)
+    arr = (moe_layer * max(n, 1))(*layers)
+    offs = None
+    if logit_offsets is not None:
+        offs = (_P * max(n, 1))(*[_dptr(o) for o in logit_offsets])
+    _check(lib().moe_stack_decode(C.byref(as_shape(shape)), arr, n, _dptr(x), offs, _dptr(topk_idx),
+                                  _dptr(topk_w), _dptr(expert_out), _dptr(y), _dptr(x_layers), _dptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "moe_stack_decode")
 
 
 def moe_layer_prefill(shape, layer: moe_layer, x, rows: int, logit_offset, topk_idx, topk_w, count, offset, perm,

@@ -61,6 +61,9 @@ constexpr int kFusedMaxG = 48;       // d_model / 64
 constexpr int kFusedGuI = 6;         // gate/up loads per lane and matrix: group pairs / 4 waves
 constexpr int kFusedRoutedGW = 3;    // routed down: groups of d_ff per wave (d_ff <= 768)
 constexpr int kFusedSharedGW = 5;    // shared down: groups of half of d_ff_shared per wave (<= 2560)
+constexpr int kXCopies = 16;         // copies of the next layer's input in the stacked decode ...
+constexpr int kXStride = 2048;       // ... 16 KiB apart (words; a copy holds d_model / 2 bf16 pairs)
+constexpr int kMaxStackLayers = 32;  // layers of one stacked-decode launch
 
 struct FusedArgs {
   const uint8_t* pool;
@@ -83,6 +86,12 @@ struct FusedArgs {
   uint64_t* eo_tag;     // [(top_k + 1) * d]: routed expert outputs, then the shared expert's second half
   uint32_t* sync;       // kFusedSyncWords
   int n_rt, n_sg, n_rg, n_rd, n_sd;  // n_sd = d / 64 second-half items, then as many combines
+  // stacked decode (k_stack_decode) only; zero for one layer:
+  uint64_t* x_tag;      // kXCopies x kXStride: the next layer's input as tagged bf16 pairs
+  int x_in, x_out;      // this layer reads its input from / writes the next layer's to x_tag
+  int arrive;           // this layer's items arrive at the epoch counters (the first layer)
+  uint16_t* x_rec;      // [d] or null: receives this layer's input (bf16)
+  int layer;            // index in the stack (timeline stamps only)
 };
 
 struct FusedSmem {
@@ -106,16 +115,18 @@ struct FusedSmem {
 };
 
 // Timeline build (QMOE_TIMELINE): thread 0 of each workgroup stamps the 100 MHz
-// real-time counter at the phase boundaries of its item into g_timeline[block][slot]
-// (kStamps slots per block; the slot meanings per item kind are listed at each
-// QMOE_STAMP). The default build compiles the stamps away.
+// real-time counter at the phase boundaries of its item into
+// g_timeline[layer][block][slot] (kStamps slots per block; the slot meanings per item
+// kind are listed at each QMOE_STAMP; F is the item's FusedArgs). The default build
+// compiles the stamps away.
 constexpr int kStamps = 8;
 #ifdef QMOE_TIMELINE
 __device__ uint64_t* g_timeline = nullptr;
 #define QMOE_STAMP(slot)                                                                        \
   do {                                                                                          \
     if (threadIdx.x == 0 && g_timeline)                                                         \
-      g_timeline[(size_t)blockIdx.x * kStamps + (slot)] = __builtin_amdgcn_s_memrealtime();     \
+      g_timeline[((size_t)F.layer * gridDim.x + blockIdx.x) * kStamps + (slot)] =               \
+          __builtin_amdgcn_s_memrealtime();                                                     \
   } while (0)
 #else
 #define QMOE_STAMP(slot) \
@@ -129,6 +140,16 @@ __device__ __forceinline__ uint32_t ld_agent_u(const uint32_t* p) {
 __device__ __forceinline__ void st_agent_u(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// threadIdx.x as a value the compiler must take as new where this is called: in the
+// stacked decode's layer loop, values derived from the thread index are then computed in
+// each layer instead of hoisted out of the loop and held (spilled) across it
+template <bool kOpaque>
+__device__ __forceinline__ int thread_index() {
+  int t = threadIdx.x;
+  if constexpr (kOpaque) asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ void put_tag(uint64_t* p, uint32_t payload, uint32_t tag) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -195,7 +216,9 @@ __device__ __forceinline__ uint32_t read_epoch(const FusedArgs& F) {
 }
 // Thread 0: this workgroup has read the epoch (the inline asm makes the increment wait
 // for the value read). No result is returned, so nothing waits for the atomic itself.
+template <bool kStack>
 __device__ __forceinline__ void arrive_epoch(const FusedArgs& F, uint32_t epoch) {
+  if (kStack && !F.arrive) return;  // a later layer of a stacked decode: arrived with the first
   uint32_t one = 1u;
   asm volatile("" : "+v"(one) : "v"(epoch));
   __hip_atomic_fetch_add(&F.sync[(kEpochCopies + blockIdx.x % kArrivalCounters) * kSyncLine], one,
@@ -203,8 +226,8 @@ __device__ __forceinline__ void arrive_epoch(const FusedArgs& F, uint32_t epoch)
 }
 // The last workgroup of the grid: waits for the arrivals of all others (blocks
 // b < gridDim.x - 1 arrive at counter b % kArrivalCounters), then clears the counters
-// and writes epoch + 1 into every copy.
-__device__ __forceinline__ void epoch_keeper(const FusedArgs& F, uint32_t epoch) {
+// and writes epoch + adv into every copy (adv = the tags the launch used: one per layer).
+__device__ __forceinline__ void epoch_keeper(const FusedArgs& F, uint32_t epoch, uint32_t adv = 1u) {
   const int tid = threadIdx.x;
   const int n = (int)gridDim.x - 1;
   if (tid < kArrivalCounters) {
@@ -220,17 +243,47 @@ __device__ __forceinline__ void epoch_keeper(const FusedArgs& F, uint32_t epoch)
   }
   __syncthreads();
   if (tid < kArrivalCounters) st_agent_u(&F.sync[(kEpochCopies + tid) * kSyncLine], 0u);
-  if (tid < kEpochCopies) st_agent_u(&F.sync[tid * kSyncLine], epoch + 1u);
+  if (tid < kEpochCopies) st_agent_u(&F.sync[tid * kSyncLine], epoch + adv);
+}
+
+// A later layer of a stacked decode: waits until the previous layer's combines have all
+// begun to hand over this layer's input. One wave polls one word per combine (the first
+// pair of its rows, in this block's copy), so that the many workgroups that wait through
+// the previous layer's tail poll d / 64 words each, not the whole input or their own
+// (later) inputs. Ends with a barrier.
+__device__ __forceinline__ void wait_x_in(const FusedArgs& F, uint32_t tag) {
+  const int tid = threadIdx.x;
+  const uint64_t* xs = F.x_tag + (size_t)(blockIdx.x % kXCopies) * kXStride;
+  if (tid < 64) {
+    for (int it = 0;; ++it) {
+      bool in = true;
+      for (int j = tid; j < F.d / 64; j += 64) in &= (uint32_t)(get_tag(xs + 32 * j) >> 32) == tag;
+      if (__all(in)) break;
+      if (it >= kSpinLimit) {
+        if (tid == 0) flag_device_error(4u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
 }
 
 // x into LDS. kRaw (router): bf16 x as stored pairs, fp32 x as values. Otherwise
 // (gate/up): bf16 pairs, or for fp32 x hi pairs at xb[0, d/2) and lo pairs at
 // xb[kFusedXWords/2, ...) with hi + lo the fp32 value to 16 significant bits;
 // then xg = sums over the 32-column halves of each group. Ends with a barrier.
-template <typename XT, bool kRaw>
-__device__ __forceinline__ void stage_x(const XT* __restrict__ x, int d, FusedSmem& S) {
-  const int tid = threadIdx.x;
-  if constexpr (sizeof(XT) == 2 || kRaw) {
+template <typename XT, bool kRaw, bool kStack>
+__device__ __forceinline__ void stage_x(const XT* __restrict__ x, const FusedArgs& F, uint32_t tag, FusedSmem& S) {
+  const int tid = threadIdx.x, d = F.d;
+  if (kStack && sizeof(XT) == 2 && F.x_in) {
+    // a later layer of a stacked decode: the previous layer's combines hand over the input
+    // as tagged bf16 pairs (this block's copy)
+    const uint64_t* xs = F.x_tag + (size_t)(blockIdx.x % kXCopies) * kXStride;
+    wait_x_in(F, tag);
+    poll_tagged<kFusedXWords / 2 / 256>([&](int i) { return xs + i; }, d / 2, tag,
+                                        [&](int i, uint32_t p) { S.xb[i] = p; });
+  } else if constexpr (sizeof(XT) == 2 || kRaw) {
     for (int i = tid; i < d * (int)sizeof(XT) / 16; i += 256)
       *reinterpret_cast<uint4*>(&S.xb[4 * i]) = ldg16(reinterpret_cast<const uint8_t*>(x) + 16 * i);
   } else {
@@ -361,10 +414,10 @@ __device__ __forceinline__ float x_at(const FusedSmem& S, int col) {
 // experts [2 item, +2): thread t takes row (t & 1), column quarter (t >> 1) & 3 and the
 // groups (t >> 3) + 32 j; products w * x are exact in fp64 (w = s q + b has at most
 // 20 significant bits, x at most 24) and the sums are fp64.
-template <typename XT>
+template <typename XT, bool kStack>
 __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __restrict__ x, int item, uint32_t tag,
                                              uint32_t epoch, FusedSmem& S) {
-  const int tid = threadIdx.x;
+  const int tid = thread_index<kStack>();
   const int G = F.d / kGroup;
   const int e0 = item * kFusedRouterE, nb = e0 / 64, row = e0 % 64 + (tid & 1);
   const int c = (tid >> 1) & 3, gs = tid >> 3;
@@ -378,8 +431,8 @@ __device__ __forceinline__ void fused_router(const FusedArgs& F, const XT* __res
     q[j] = *reinterpret_cast<const u32x4_t*>(t + c * 1024 + row * 16);
     sb[j] = ldg4(t + kTile8Codes + row * 4);
   }
-  if (tid == 0) arrive_epoch(F, epoch);  // before the first wait, which covers it
-  stage_x<XT, true>(x, F.d, S);
+  if (tid == 0) arrive_epoch<kStack>(F, epoch);  // before the first wait, which covers it
+  stage_x<XT, true, kStack>(x, F, tag, S);
   QMOE_STAMP(1);  // router: weights and x in
   double acc = 0.0;
 #pragma unroll
@@ -460,10 +513,10 @@ __device__ __forceinline__ float half_dot(const u32x4_t& q, const uint32_t* xp, 
 // Rows [16 q4, +16) of 64-row block nb of the gate and up matrices, whole reduction.
 // Lane l of wave w: group pair (w + 4 i), group 2 (w + 4 i) + (l >> 5), column half
 // (l >> 4) & 1, row l & 15: each wavefront load is 4 runs of 256 contiguous bytes.
-template <typename XT>
+template <typename XT, bool kStack>
 __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __restrict__ x, int u, bool routed,
                                              uint32_t tag, uint32_t epoch, FusedSmem& S) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = thread_index<kStack>(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = F.d / kGroup;
   int slot = F.top_k, Fd = F.fs;
@@ -494,20 +547,24 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
   if (!routed) {
     // the shared expert's weights start streaming once the router items have published
     // their keys: the router's own loads, which head the chain, then meet an idle
-    // memory system instead of the shared expert's 10 MB
-    const uint64_t* lk = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride + kLgKeys;
-    poll_tagged<1>([&](int i) { return lk + i; }, F.E, tag, [&](int i, uint32_t p) { S.kp[i] = p; });
+    // memory system instead of the shared expert's 10 MB. In a later layer of a stacked
+    // decode they stream at once instead, while the previous layer finishes (its tail
+    // leaves the memory system idle).
+    if (!(kStack && F.x_in)) {
+      const uint64_t* lk = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride + kLgKeys;
+      poll_tagged<1>([&](int i) { return lk + i; }, F.E, tag, [&](int i, uint32_t p) { S.kp[i] = p; });
+    }
     QMOE_STAMP(1);  // shared gate/up: the router has published
     load(blob);
-    if (tid == 0) arrive_epoch(F, epoch);
+    if (tid == 0) arrive_epoch<kStack>(F, epoch);
   }
   const uint32_t slot_entry = (routed && tid < F.E) ? F.slot_table[tid] : 0u;
-  stage_x<XT, false>(x, F.d, S);
+  stage_x<XT, false, kStack>(x, F, tag, S);
   if (routed) {
     // the arrival goes after the weight loads: no wait on the ticket's path covers it
     blob = routed_blob(F, slot, tag, slot_entry, S);
     if (blob) load(blob);
-    if (tid == 0) arrive_epoch(F, epoch);
+    if (tid == 0) arrive_epoch<kStack>(F, epoch);
   }
   float acc[2] = {0.0f, 0.0f};
   if (blob) {
@@ -657,14 +714,23 @@ __device__ __forceinline__ float gather_h(const uint64_t* src, int j0, int j1, u
   return sc;
 }
 
+// exp as a call: inlined into the layer loop of the stacked decode, its constants are
+// hoisted out of the loop and held (spilled) across it
+__device__ __attribute__((noinline)) double exp_call(double v) { return exp(v); }
+
 // The picks and their softmax weights into S.sel_e, S.selw (fp64 softmax over the
 // picked logits, fixed summation order).
+template <bool kStack>
 __device__ __forceinline__ void pick_weights(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
-  const int tid = threadIdx.x, lane = tid & 63, k = F.top_k;
+  const int tid = thread_index<kStack>(), lane = tid & 63, k = F.top_k;
   rank_logits(F, tag, S);
   load_logits(F, tag, S);  // the picked logits for the weights (long published by now)
   if (tid < 64) {
-    const double ex = lane < k ? exp(S.lg[S.sel_e[lane]] - S.lg[S.sel_e[0]]) : 0.0;
+    double ex = 0.0;
+    if (lane < k) {
+      const double v = S.lg[S.sel_e[lane]] - S.lg[S.sel_e[0]];
+      ex = kStack ? exp_call(v) : exp(v);
+    }
     double sum = 0.0;
     for (int t = 0; t < k; ++t) sum += __shfl(ex, t, 64);
     if (lane < k) S.selw[lane] = (float)(ex / sum);
@@ -673,9 +739,12 @@ __device__ __forceinline__ void pick_weights(const FusedArgs& F, uint32_t tag, F
 
 // y for rows [64 ob, +64) once the picks are known (pick_weights): r (wave 0) is the
 // shared expert's first half for the row; adds its second half, then the routed
-// outputs weighted by the softmax over the picks, in pick order.
-__device__ __forceinline__ void fused_combine(const FusedArgs& F, int ob, float r, uint32_t tag, FusedSmem& S) {
-  const int tid = threadIdx.x, lane = tid & 63, k = F.top_k;
+// outputs weighted by the softmax over the picks, in pick order. old (wave 0): the
+// residual's bf16 value for the row (when there is a residual).
+template <bool kStack>
+__device__ __forceinline__ void fused_combine(const FusedArgs& F, int ob, float r, uint16_t old, uint32_t tag,
+                                              FusedSmem& S) {
+  const int tid = thread_index<kStack>(), lane = tid & 63, k = F.top_k;
   poll_tagged<5>([&](int i) { return F.eo_tag + (size_t)(i >> 6) * F.d + ob * 64 + (i & 63); }, 64 * (k + 1), tag,
                  [&](int i, uint32_t p) { S.eo[i >> 6][i & 63] = __uint_as_float(p); });
   __syncthreads();
@@ -684,8 +753,23 @@ __device__ __forceinline__ void fused_combine(const FusedArgs& F, int ob, float 
     float yv = r + S.eo[k][lane];
     for (int s = 0; s < k; ++s) yv = fmaf(S.selw[s], S.eo[s][lane], yv);
     const int n = ob * 64 + lane;
-    F.y[n] = yv;
-    if (F.residual) F.residual[n] = (uint16_t)f32_to_bf16_bits(bf16_to_f32(F.residual[n]) + yv);
+    if (F.y) F.y[n] = yv;
+    if (F.residual) {
+      const uint32_t nv = f32_to_bf16_bits(bf16_to_f32(old) + yv);
+      F.residual[n] = (uint16_t)nv;
+      if (kStack && F.x_rec) F.x_rec[n] = old;
+      if (kStack && F.x_out) {
+        // the next layer's input as tagged pairs: lanes 2j and 2j + 1 hold the pair, each
+        // writes half of the copies
+        // both shuffles run in every lane (a shuffle reads lanes that take part in it)
+        const uint32_t up = (uint32_t)__shfl_down((int)nv, 1, 64);
+        const uint32_t dn = (uint32_t)__shfl_up((int)nv, 1, 64);
+        const uint32_t pair = (lane & 1) ? (dn | (nv << 16)) : (nv | (up << 16));
+#pragma unroll
+        for (int c = lane & 1; c < kXCopies; c += 2)
+          put_tag(&F.x_tag[(size_t)c * kXStride + (n >> 1)], pair, tag + 1u);
+      }
+    }
     if (ob == 0 && lane < k) {
       F.idx_out[lane] = S.sel_e[lane];
       F.w_out[lane] = S.selw[lane];
@@ -698,10 +782,10 @@ __device__ __forceinline__ void fused_combine(const FusedArgs& F, int ob, float 
 // kind 1: the shared expert's second half -> tagged partial; kind 2: the shared
 // expert's first half, then the combine of the rows. The weights stream as soon as
 // the expert is known, while h is still being produced.
-template <int GW>
+template <int GW, bool kStack>
 __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, uint32_t tag, uint32_t epoch,
                                            FusedSmem& S) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = thread_index<kStack>(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NBd = F.d / 64;
   int slot = F.top_k, ob = u, Fd = F.fs;
@@ -713,6 +797,12 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
   const int Gin = Fd / kGroup, Gh = (Gin + 1) / 2;
   const int g0 = kind == 1 ? Gh : 0, g1 = kind == 2 ? Gh : Gin;
   const uint32_t slot_entry = (kind == 0 && tid < F.E) ? F.slot_table[tid] : 0u;
+  // the combine's residual rows, read now so that the read is not on the tail of the chain
+  // (in a stacked decode this thread wrote them itself in the previous layer)
+  const uint16_t old = (kind == 2 && F.residual && tid < 64) ? F.residual[ob * 64 + lane] : (uint16_t)0;
+  // a later layer of a stacked decode: the waits for the keys and for h start once this
+  // layer's input is in (they would otherwise poll through the previous layer's tail)
+  if (kStack && kind == 0 && F.x_in) wait_x_in(F, tag);
   const uint8_t* blob = kind == 0 ? routed_blob(F, slot, tag, slot_entry, S) : F.shared_blob;
   RowLoads<GW> w;
   const uint8_t* rowblock = blob ? blob + 2 * m4_bytes(Fd, F.d) + (uint64_t)ob * Gin * kTile4 : nullptr;
@@ -722,15 +812,21 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
     // a routed expert's down weights wait until its h starts to come in, so that they do
     // not take memory bandwidth from the gate/up loads h depends on; they arrive while
     // the rest of h is produced
-    if (tid == 0) arrive_epoch(F, epoch);
+    if (tid == 0) arrive_epoch<kStack>(F, epoch);
     sc = gather_h<true>(hsrc, g0 * kGroup, g1 * kGroup, tag, S, [&] {
       QMOE_STAMP(3);  // routed down: the first values of h in
       if (rowblock) w.load(rowblock, g0, g1, wave, lane);
     });
   } else {
-    if (rowblock) w.load(rowblock, g0, g1, wave, lane);
-    if (tid == 0) arrive_epoch(F, epoch);
-    if (kind == 2) pick_weights(F, tag, S);  // the logits are out long before the shared h
+    // in a stacked decode the combine ranks the picks before its weights stream: the
+    // ranking's registers and the weights' then need not be held at once (the layer
+    // loop leaves too few for both), and both are done long before the shared h is in
+    const bool late = kStack && kind == 2;
+    if (rowblock && !late) w.load(rowblock, g0, g1, wave, lane);
+    if (tid == 0) arrive_epoch<kStack>(F, epoch);
+    if (kStack && F.x_in) wait_x_in(F, tag);
+    if (kind == 2) pick_weights<kStack>(F, tag, S);  // the logits are out long before the shared h
+    if (rowblock && late) w.load(rowblock, g0, g1, wave, lane);
     sc = gather_h(hsrc, g0 * kGroup, g1 * kGroup, tag, S);
   }
   QMOE_STAMP(4);  // down, combine: all of h in
@@ -738,10 +834,10 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
   const float r = reduce_waves4(acc, S.red[0], wave, lane) * (1.0f / sc);  // exact: sc is a power of two
   QMOE_STAMP(5);  // down, combine: dot products done
   if (kind == 2) {
-    fused_combine(F, ob, r, tag, S);
+    fused_combine<kStack>(F, ob, r, old, tag, S);
   } else if (wave == 0) {
     const int n = ob * 64 + lane;
-    if (kind == 0) F.expert_out[(size_t)slot * F.d + n] = r;
+    if (kind == 0 && F.expert_out) F.expert_out[(size_t)slot * F.d + n] = r;
     put_tag(&F.eo_tag[(size_t)slot * F.d + n], __float_as_uint(r), tag);
   }
   QMOE_STAMP(7);  // down: outputs stored; combine: y stored
@@ -753,24 +849,160 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
 // take the lowest blocks, so they are dispatched first and spread over all eight XCDs
 // (blocks are dealt to the XCDs round robin). Any placement is correct (all blocks are
 // resident at once); packing the router items onto two XCDs measured 0.66 us slower.
+// the work item of this block for one layer
+template <typename XT>
+__device__ __forceinline__ void fused_item(const FusedArgs& F, const XT* __restrict__ x, uint32_t tag, uint32_t epoch,
+                                           FusedSmem& S) {
+  int b = blockIdx.x;
+  if (b < F.n_rt) {
+    fused_router<XT, false>(F, x, b, tag, epoch, S);
+  } else if ((b -= F.n_rt) < F.n_sg + F.n_rg) {
+    const bool routed = b >= F.n_sg;
+    fused_gateup<XT, false>(F, x, routed ? b - F.n_sg : b, routed, tag, epoch, S);
+  } else if ((b -= F.n_sg + F.n_rg) < F.n_rd) {
+    fused_down<kFusedRoutedGW, false>(F, b, 0, tag, epoch, S);
+  } else {
+    b -= F.n_rd;
+    fused_down<kFusedSharedGW, false>(F, b < F.n_sd ? b : b - F.n_sd, b < F.n_sd ? 1 : 2, tag, epoch, S);
+  }
+}
+
 template <typename XT>
 __global__ __launch_bounds__(256, 4) void k_decode_fused(FusedArgs F, const XT* __restrict__ x) {
   __shared__ FusedSmem S;
   QMOE_STAMP(0);  // every item: started
   const uint32_t epoch = read_epoch(F);
-  const uint32_t tag = epoch + 1u;
   if (blockIdx.x == gridDim.x - 1) return epoch_keeper(F, epoch);
+  fused_item(F, x, epoch + 1u, epoch, S);
+}
+
+// ------------------------------------------------------------------ stacked decode
+
+// One layer of a stack: its weights (every layer may have its own pool and table).
+struct StackLayer {
+  const uint8_t* pool;
+  const uint32_t* slot_table;
+  const uint8_t* router_blob;
+  const uint8_t* shared_blob;
+  const float* offset;  // [E] or null
+  uint64_t stride, n_blobs;
+};
+
+struct StackArgs {
+  FusedArgs F;  // the shape, the workspace words and the outputs of layer 0
+  int n_layers;
+  StackLayer layer[kMaxStackLayers];
+};
+
+// One decode row through n_layers blocks in ONE launch, x <- bf16(x + y) after each.
+// Every workgroup keeps its work item from layer to layer, so an item starts the next
+// layer as soon as it is done with this one: routing-independent weights (the router's,
+// the shared expert's gate/up and down) stream while the previous layer finishes, and
+// only the wait for the next layer's input remains. The combines hand the next input
+// over as tagged bf16 pairs (kXCopies copies); layer l tags its words epoch + 1 + l and
+// the keeper advances the epoch by n_layers. Every hand-off region is reused from layer
+// to layer: a layer's words are written only after the next input is complete, which
+// every reader of the previous layer's words precedes.
+// a uniform pointer the compiler must treat as new in every layer: addresses derived
+// from the workspace pointers are then computed where they are used instead of hoisted
+// out of the layer loop and held in registers across it (which spills)
+template <typename T>
+__device__ __forceinline__ T* per_layer(T* p) {
+#if __HIP_DEVICE_COMPILE__
+  // laundered as a global pointer, so that accesses through it stay global (not flat)
+  __attribute__((address_space(1))) T* g = (__attribute__((address_space(1))) T*)p;
+  asm volatile("" : "+s"(g));
+  return (T*)g;
+#else
+  return p;
+#endif
+}
+
+__device__ __forceinline__ int per_layer_i(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// The arguments of layer l of a stacked decode, read through a pointer to the kernel's
+// argument block (StackArgs is the kernel's first argument, so at offset 0 of the
+// kernarg segment) that the compiler must treat as new in every layer: they are then
+// loaded (scalar loads) in each layer instead of held in registers across the loop.
+#if __HIP_DEVICE_COMPILE__
+typedef const __attribute__((address_space(4))) StackArgs KernargStackArgs;
+#else
+typedef const StackArgs KernargStackArgs;
+#endif
+__device__ __forceinline__ FusedArgs stack_layer_args(int l) {
+  KernargStackArgs* Ap = (KernargStackArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(Ap));
+  KernargStackArgs& A = *Ap;
+  const auto& L = A.layer[l];
+  const int k = A.F.top_k, d = A.F.d;
+  FusedArgs F = A.F;
+  F.lg_tag = per_layer(F.lg_tag);
+  F.h_tag = per_layer(F.h_tag);
+  F.eo_tag = per_layer(F.eo_tag);
+  F.x_tag = per_layer(F.x_tag);
+  F.sync = per_layer(F.sync);
+  F.pool = L.pool;
+  F.slot_table = L.slot_table;
+  F.router_blob = L.router_blob;
+  F.shared_blob = L.shared_blob;
+  F.offset = L.offset;
+  F.stride = L.stride;
+  F.n_blobs = L.n_blobs;
+  F.arrive = l == 0;
+  F.x_in = l > 0;
+  F.x_out = l + 1 < A.n_layers;
+  F.idx_out = A.F.idx_out + (size_t)l * k;
+  F.w_out = A.F.w_out + (size_t)l * k;
+  F.expert_out = A.F.expert_out ? A.F.expert_out + (size_t)l * k * d : nullptr;
+  F.y = A.F.y ? A.F.y + (size_t)l * d : nullptr;
+  F.x_rec = A.F.x_rec ? A.F.x_rec + (size_t)l * d : nullptr;
+  F.layer = l;
+  F.d = per_layer_i(F.d);
+  F.f = per_layer_i(F.f);
+  F.fs = per_layer_i(F.fs);
+  F.E = per_layer_i(F.E);
+  F.top_k = per_layer_i(F.top_k);
+  F.fmax = per_layer_i(F.fmax);
+  F.n_rt = per_layer_i(F.n_rt);
+  F.n_sg = per_layer_i(F.n_sg);
+  F.n_rg = per_layer_i(F.n_rg);
+  F.n_rd = per_layer_i(F.n_rd);
+  F.n_sd = per_layer_i(F.n_sd);
+  return F;
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256, 4) void k_stack_decode(StackArgs A, const XT* __restrict__ x) {
+  __shared__ FusedSmem S;
+  const uint32_t epoch = read_epoch(A.F);
+  if (blockIdx.x == gridDim.x - 1) return epoch_keeper(A.F, epoch, (uint32_t)A.n_layers);
+  // one loop per item kind, so that a loop holds only its own kind's code
+  auto layers = [&](auto item) __attribute__((always_inline)) {
+    for (int l = 0; l < A.n_layers; ++l) {
+      const FusedArgs F = stack_layer_args(l);
+      QMOE_STAMP(0);  // every item: started (the layer)
+      item(F, epoch + 1u + (uint32_t)l);
+      __syncthreads();  // the next layer's item reuses the LDS
+    }
+  };
+  const FusedArgs& F0 = A.F;
   int b = blockIdx.x;
-  if (b < F.n_rt) {
-    fused_router(F, x, b, tag, epoch, S);
-  } else if ((b -= F.n_rt) < F.n_sg + F.n_rg) {
-    const bool routed = b >= F.n_sg;
-    fused_gateup(F, x, routed ? b - F.n_sg : b, routed, tag, epoch, S);
-  } else if ((b -= F.n_sg + F.n_rg) < F.n_rd) {
-    fused_down<kFusedRoutedGW>(F, b, 0, tag, epoch, S);
+  if (b < F0.n_rt) {
+    layers([&](const FusedArgs& F, uint32_t tag) { fused_router<XT, true>(F, x, b, tag, epoch, S); });
+  } else if ((b -= F0.n_rt) < F0.n_sg) {
+    layers([&](const FusedArgs& F, uint32_t tag) { fused_gateup<XT, true>(F, x, b, false, tag, epoch, S); });
+  } else if ((b -= F0.n_sg) < F0.n_rg) {
+    layers([&](const FusedArgs& F, uint32_t tag) { fused_gateup<XT, true>(F, x, b, true, tag, epoch, S); });
+  } else if ((b -= F0.n_rg) < F0.n_rd) {
+    layers([&](const FusedArgs& F, uint32_t tag) { fused_down<kFusedRoutedGW, true>(F, b, 0, tag, epoch, S); });
+  } else if ((b -= F0.n_rd) < F0.n_sd) {
+    layers([&](const FusedArgs& F, uint32_t tag) { fused_down<kFusedSharedGW, true>(F, b, 1, tag, epoch, S); });
   } else {
-    b -= F.n_rd;
-    fused_down<kFusedSharedGW>(F, b < F.n_sd ? b : b - F.n_sd, b < F.n_sd ? 1 : 2, tag, epoch, S);
+    b -= F0.n_sd;
+    layers([&](const FusedArgs& F, uint32_t tag) { fused_down<kFusedSharedGW, true>(F, b, 2, tag, epoch, S); });
   }
 }
 

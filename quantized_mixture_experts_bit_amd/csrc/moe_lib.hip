@@ -72,9 +72,9 @@ size_t fused_h_stride(const moe_shape* s) {
 // the shape only (zeroed once, left at zero by every call), so layouts for
 // different row counts never place a counter where another call kept data.
 struct Ws {
-  size_t gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, router_partial, gu_partial, h_hi,
+  size_t gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, fused_x, router_partial, gu_partial, h_hi,
       h_lo, h_gsum,
-      shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, pf_xg, total;
+      shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, pf_xg, st_eo, st_y, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -95,6 +95,7 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.fused_lg = take(sizeof(uint64_t) * kLgCopies * kLgStride);
   w.fused_h = take(sizeof(uint64_t) * kHCopies * fused_h_stride(s));
   w.fused_eo = take(sizeof(uint64_t) * (size_t)(k + 1) * d);
+  w.fused_x = take(sizeof(uint64_t) * kXCopies * kXStride);
   w.router_partial = take(sizeof(double) * kRouterSplits * R * s->n_experts);
   w.gu_partial = take(sizeof(float) * (size_t)(k + 1) * 2 * dc.nbmax * dc.P * 64);
   w.h_hi = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
@@ -108,6 +109,9 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.pf_Hh = take(sizeof(uint16_t) * R * ((size_t)k * s->d_ff + s->d_ff_shared));
   w.pf_hsc = take(sizeof(float) * R * (k + 1));
   w.pf_xg = take(sizeof(float) * R * ((d / 64 + 3) & ~3));  // rows padded to a multiple of 4 groups
+  // the stacked decode's per-layer outputs the caller does not keep (layer-by-layer path)
+  w.st_eo = take(sizeof(float) * (size_t)k * d);
+  w.st_y = take(sizeof(float) * (size_t)d);
   w.total = o;
   return w;
 }
@@ -220,16 +224,18 @@ int fused_capacity() {
   return cap[dev];
 }
 
-// One persistent launch for the whole decode row, when the grid fits on the chip;
-// returns false (nothing launched) otherwise.
-template <typename XT>
-bool launch_decode_fused(const moe_shape* s, const moe_layer* L, const XT* x, const float* off, int32_t* idx,
-                         float* w, float* expert_out, float* y, uint16_t* residual, void* ws, const Ws& W,
-                         hipStream_t st) {
-  // limits of the fused kernel's register and LDS tiling (see decode_fused.h)
+// whether the whole-block decode kernel's tiling takes the shape (see decode_fused.h)
+bool fused_shape_ok(const moe_shape* s, bool f32_x) {
   const int d = s->d_model, f = s->d_ff, fs = s->d_ff_shared;
   if (d / 64 > kFusedMaxG || f > 64 * 4 * kFusedRoutedGW || fs > 2 * 64 * 4 * kFusedSharedGW) return false;
-  if (sizeof(XT) == 4 && d > kFusedXWords) return false;
+  return !(f32_x && d > kFusedXWords);
+}
+
+// arguments of the whole-block decode kernel for one layer (the grid is
+// n_rt + n_sg + n_rg + n_rd + 2 n_sd + 1 workgroups)
+FusedArgs fused_args(const moe_shape* s, const moe_layer* L, const float* off, int32_t* idx, float* w,
+                     float* expert_out, float* y, uint16_t* residual, void* ws, const Ws& W) {
+  const int d = s->d_model, f = s->d_ff, fs = s->d_ff_shared;
   FusedArgs F;
   memset(&F, 0, sizeof F);
   F.pool = L->pool;
@@ -260,7 +266,22 @@ bool launch_decode_fused(const moe_shape* s, const moe_layer* L, const XT* x, co
   F.n_rg = s->top_k * (f / kFusedRows);
   F.n_rd = s->top_k * (d / 64);
   F.n_sd = d / 64;
-  const int grid = F.n_rt + F.n_sg + F.n_rg + F.n_rd + 2 * F.n_sd + 1;  // + the epoch keeper
+  F.x_tag = at<uint64_t>(ws, W.fused_x);
+  F.arrive = 1;
+  return F;
+}
+
+int fused_grid(const FusedArgs& F) { return F.n_rt + F.n_sg + F.n_rg + F.n_rd + 2 * F.n_sd + 1; }  // + the keeper
+
+// One persistent launch for the whole decode row, when the grid fits on the chip;
+// returns false (nothing launched) otherwise.
+template <typename XT>
+bool launch_decode_fused(const moe_shape* s, const moe_layer* L, const XT* x, const float* off, int32_t* idx,
+                         float* w, float* expert_out, float* y, uint16_t* residual, void* ws, const Ws& W,
+                         hipStream_t st) {
+  if (!fused_shape_ok(s, sizeof(XT) == 4)) return false;
+  const FusedArgs F = fused_args(s, L, off, idx, w, expert_out, y, residual, ws, W);
+  const int grid = fused_grid(F);
   if (grid > fused_capacity<XT>()) return false;
   k_decode_fused<XT><<<grid, 256, 0, st>>>(F, x);
   return true;
@@ -311,6 +332,29 @@ int resident_blocks(K kernel, int* cache) {
     cache[dev] = std::max(1, per_cu * cus);
   }
   return cache[dev];
+}
+
+// The stacked decode in one launch, when the shape fits the fused kernel's tiling and
+// the grid fits on the chip; returns false (nothing launched) otherwise.
+bool launch_stack_decode(const moe_shape* s, const moe_layer* layers, int n_layers, uint16_t* x,
+                         const float* const* offsets, int32_t* idx, float* w, float* expert_out, float* y,
+                         uint16_t* x_layers, void* ws, const Ws& W, hipStream_t st) {
+  static int cap[64];
+  if (n_layers > kMaxStackLayers || !fused_shape_ok(s, false)) return false;
+  StackArgs A;
+  memset(&A, 0, sizeof A);
+  A.F = fused_args(s, &layers[0], nullptr, idx, w, expert_out, y, x, ws, W);
+  A.F.x_rec = x_layers;
+  A.n_layers = n_layers;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer& L = layers[l];
+    A.layer[l] = StackLayer{L.pool, L.slot_table, L.router_blob, L.shared_blob, offsets ? offsets[l] : nullptr,
+                            L.blob_stride, L.n_blobs};
+  }
+  const int grid = fused_grid(A.F);
+  if (grid > resident_blocks(k_stack_decode<uint16_t>, cap)) return false;
+  k_stack_decode<uint16_t><<<grid, 256, 0, st>>>(A, x);
+  return true;
 }
 
 // grid of a persistent GEMM launch: what the chip holds at once (a multiple of the
@@ -581,6 +625,35 @@ moe_status moe_layer_decode_noalloc(const moe_shape* s, const moe_layer* L, cons
   void* scratch_ptr = nullptr;
   if ((st = static_scratch(hs, &scratch_ptr)) != MOE_OK) return st;
   layer_decode(s, L, x, dt, off, idx, w, expert_out, y, residual, scratch_ptr, static_layout(), hs);
+  return launched();
+}
+
+moe_status moe_stack_decode(const moe_shape* s, const moe_layer* layers, int32_t n_layers, uint16_t* x,
+                            const float* const* offsets, int32_t* idx, float* w, float* expert_out, float* y,
+                            uint16_t* x_layers, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_common(s, x, MOE_BF16, 1, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (!layers || n_layers < 0) return MOE_ERR_INVALID_ARG;
+  if (n_layers == 0) return MOE_OK;
+  for (int l = 0; l < n_layers; ++l)
+    if ((st = check_layer(s, &layers[l], true, true, true)) != MOE_OK) return st;
+  if (!idx || !w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(expert_out) || !aligned16(y) || !aligned16(x_layers)) return MOE_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  const Ws W = ws_layout(s, 1);
+  if (launch_stack_decode(s, layers, n_layers, x, offsets, idx, w, expert_out, y, x_layers, ws, W, hs))
+    return launched();
+  // layer by layer (a shape or a layer count the one-launch kernel does not take)
+  const int k = s->top_k, d = s->d_model;
+  for (int l = 0; l < n_layers; ++l) {
+    if (x_layers &&
+        hipMemcpyAsync(x_layers + (size_t)l * d, x, sizeof(uint16_t) * d, hipMemcpyDeviceToDevice, hs) != hipSuccess)
+      return MOE_ERR_HIP;
+    float* eo = expert_out ? expert_out + (size_t)l * k * d : at<float>(ws, W.st_eo);
+    float* yl = y ? y + (size_t)l * d : at<float>(ws, W.st_y);
+    layer_decode(s, &layers[l], x, MOE_BF16, offsets ? offsets[l] : nullptr, idx + (size_t)l * k,
+                 w + (size_t)l * k, eo, yl, x, ws, W, hs);
+  }
   return launched();
 }
 

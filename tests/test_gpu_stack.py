@@ -308,3 +308,65 @@ def test_stack_prefill_graph_replay_bit_exact(live):
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(h), want), "replay %d" % rep
     assert q.moe_check_device_error() == 0
+
+
+@pytest.mark.parametrize("which", ["literal", "live"])
+def test_stack_decode_one_launch_matches_layer_calls(request, which):
+    """moe_stack_decode (all 30 layers in one launch) gives the bits of the 30
+    moe_layer_decode calls the fixture recorded: every layer's input, picks, weights,
+    unweighted expert outputs and y, and the final row. With those equal, the
+    teacher-forced oracle checks above hold for the one-launch stack as well."""
+    st = request.getfixturevalue(which)
+    shape, layers = st["shape"], st["layers"]
+    k, d, L = shape.top_k, shape.d_model, N_LAYERS
+    x = to_dev_x(st["x0_dec"]).clone()
+    idx, w = empty_i32(L, k), empty_f32(L, k)
+    eo, y = empty_f32(L, k, d), empty_f32(L, d)
+    xl = torch.empty(L, d, dtype=torch.bfloat16, device=device())
+    q.moe_stack_decode(shape, [dl.c for dl in layers], x, None, idx, w, eo, y, xl, st["ws_dec"])
+    torch.cuda.synchronize()
+    assert q.moe_check_device_error() == 0
+    xl_b, idx_n, w_n, eo_n, y_n = bf16_bits(xl), idx.cpu().numpy(), w.cpu().numpy(), eo.cpu().numpy(), y.cpu().numpy()
+    for l, r in enumerate(st["rec"]):
+        c = r["dec"]
+        assert np.array_equal(xl_b[l], c["x"][0]), "layer %d input" % l
+        assert np.array_equal(idx_n[l], c["idx"][0]), "layer %d picks" % l
+        assert np.array_equal(w_n[l].view(np.uint32), c["w"][0].view(np.uint32)), "layer %d weights" % l
+        assert np.array_equal(eo_n[l].view(np.uint32), c["eo"][0].view(np.uint32)), "layer %d expert outputs" % l
+        assert np.array_equal(y_n[l].view(np.uint32), c["y"][0].view(np.uint32)), "layer %d y" % l
+    assert np.array_equal(bf16_bits(x)[0], st["rec"][-1]["dec"]["h"][0])
+
+
+def test_stack_decode_graph_replay_bit_exact(live):
+    """The one-launch stack captured in a HIP graph replays to the eager bits, with eager
+    calls between the replays."""
+    st = live
+    shape, layers = st["shape"], st["layers"]
+    k, d, L = shape.top_k, shape.d_model, N_LAYERS
+    cl = [dl.c for dl in layers]
+    idx, w, y = empty_i32(L, k), empty_f32(L, k), empty_f32(L, d)
+    h = torch.empty(1, d, dtype=torch.bfloat16, device=device())
+    x0 = to_dev_x(st["x0_dec"])
+    want = st["rec"][-1]["dec"]["h"]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        h.copy_(x0)
+        q.moe_stack_decode(shape, cl, h, None, idx, w, None, y, None, st["ws_dec"], stream=s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            q.moe_stack_decode(shape, cl, h, None, idx, w, None, y, None, st["ws_dec"], stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        h.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(h), want), "replay %d" % rep
+        # an eager call between the replays
+        h.copy_(x0)
+        q.moe_stack_decode(shape, cl, h, None, idx, w, None, y, None, st["ws_dec"])
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(h), want), "eager after replay %d" % rep
+    assert q.moe_check_device_error() == 0
