@@ -243,6 +243,56 @@ def decode_timeline(q, shape, run_step, n_steps, dev):
     return out
 
 
+def stack_timeline(q, shape, run_stack, n_layers, n_steps, dev):
+    """Per-phase times of the one-launch stacked decode from the timeline build: for
+    layers 1.. (whose items start while the previous layer finishes), each phase in us
+    from the previous layer's last y store, as the median workgroup / slowest workgroup,
+    medians over the layers and the n_steps steps; layer 0 from the first start."""
+    import ctypes as C
+    import numpy as np
+    import torch
+    E, k, d, f, fs = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff, shape.d_ff_shared
+    n = {"router": E // 2, "shared gate/up": fs // 16, "routed gate/up": k * (f // 16), "routed down": k * (d // 64),
+         "shared down": d // 64, "combine": d // 64}
+    grid = sum(n.values()) + 1
+    buf = torch.zeros(n_layers * grid * 8, dtype=torch.int64, device=dev)
+    fn = q.lib().moe_debug_set_timeline
+    fn.restype, fn.argtypes = C.c_int, [C.c_void_p]
+    assert fn(buf.data_ptr()) == 0
+    slots = dict(TIMELINE_SLOTS)
+    per = {kind: {slot: [] for slot in sl} for kind, sl in slots.items()}
+    first = {kind: {slot: [] for slot in sl} for kind, sl in slots.items()}
+    ends = []
+    for _ in range(n_steps):
+        buf.zero_()
+        run_stack()
+        torch.cuda.synchronize()
+        t = buf.cpu().numpy().reshape(n_layers, grid, 8).astype(np.float64) / 100.0  # 100 MHz ticks -> us
+        t0 = t[0, :grid - 1, 0].min()
+        b0 = grid - 1 - n["combine"]
+        y_end = t[:, b0:grid - 1, 7].max(axis=1)  # each layer's last y store
+        ends.append(np.diff(y_end))
+        b = 0
+        for kind, cnt in n.items():
+            for slot in slots[kind]:
+                v = t[:, b:b + cnt, slot]
+                first[kind][slot].append((float(np.median(v[0] - t0)), float((v[0] - t0).max())))
+                rel = v[1:] - y_end[:-1, None]
+                per[kind][slot].append((float(np.median(np.median(rel, axis=1))), float(np.median(rel.max(axis=1)))))
+            b += cnt
+    assert fn(None) == 0
+    out = {"layers": n_layers, "us_per_layer_median": float(np.median(np.concatenate(ends)))}
+    for kind, sl in slots.items():
+        out[kind] = {"items": n[kind]}
+        for slot, name in sl.items():
+            a = np.asarray(per[kind][slot])
+            a0 = np.asarray(first[kind][slot])
+            out[kind][name] = {"median_us": float(np.median(a[:, 0])), "slowest_us": float(np.median(a[:, 1])),
+                               "layer0_median_us": float(np.median(a0[:, 0])),
+                               "layer0_slowest_us": float(np.median(a0[:, 1]))}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,8 +313,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the streaming-read and bf16 GEMM ceilings")
     ap.add_argument("--timeline", type=int, default=0, metavar="STEPS",
-                    help="also record the decode kernel's per-phase timeline over STEPS eager steps (needs the "
-                         "timeline build: QMOE_LIB=.../libqmoe_timeline.so, from build.py --timeline)")
+                    help="also record the per-phase timelines of the decode kernel and of the one-launch stack "
+                         "over STEPS eager steps each (needs the timeline build: "
+                         "QMOE_LIB=.../libqmoe_timeline.so, from build.py --timeline)")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="rows in the oracle's timed CPU sample")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes 5 times (counter calibration) and exit")
@@ -353,7 +404,7 @@ def main():
                dec_tok_s, dec_bw / 1e12, 100 * dec_bw / HBM_PEAK, dec_flagged, steps_per_graph))
 
     timeline = None
-    if args.timeline > 0:
+    if args.timeline > 0 and not args.no_decode:
         timeline = decode_timeline(q, shape, decode_step, args.timeline, dev)
         log("decode timeline (us from the first workgroup's start; median workgroup / slowest workgroup, "
             "medians over %d steps):" % args.timeline)
@@ -474,6 +525,17 @@ def main():
             stack_decode()
         sd_per = time_replays(gsd, sd_rep, args.warmup)
         sd_ms = sum(sd_per) / sd_rep
+        sd_timeline = None
+        if args.timeline > 0:
+            sd_timeline = stack_timeline(q, shape, stack_decode, NL, args.timeline, dev)
+            log("stack decode timeline, layers 1..%d (us from the previous layer's last y; median workgroup / slowest "
+                "workgroup, medians over layers and %d steps), %.2f us per layer:"
+                % (NL - 1, args.timeline, sd_timeline["us_per_layer_median"]))
+            for kind, rec in sd_timeline.items():
+                if isinstance(rec, dict):
+                    log("  %-15s (%3d items) " % (kind, rec["items"]) + "; ".join(
+                        "%s %.2f / %.2f" % (name, v["median_us"], v["slowest_us"]) for name, v in rec.items()
+                        if name != "items"))
         sd_bytes = NL * dbytes
         # prefill: chunks of RS rows through NL layers, Zipf-skewed routing per layer
         RS = args.stack_rows
@@ -519,6 +581,7 @@ def main():
                 "value": 1000.0 / sd_ms, "unit": "tokens/s", "ms_per_token": sd_ms, "tokens": sd_rep,
                 "per_token": spread(sd_per, 1),
                 "ms_per_token_one_launch_per_layer": sl_ms,
+                "timeline": sd_timeline,
                 "roofline": {"bound": "hbm", "algorithmic_bytes_per_token": sd_bytes,
                              "achieved": sd_bytes / (sd_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                              "frac": sd_bytes / (sd_ms * 1e-3) / HBM_PEAK},
@@ -554,6 +617,10 @@ def main():
             host.load_layer(l, synth.make_layer(shape, seed=0, layer=l))
         store = TieredStore(host, args.cache_slots, dev)
         cl = [store.layer(l, dls[l].router, dls[l].shared) for l in range(NLc)]
+        # a second store over the same host tier: the overlapped flow runs the same tokens from
+        # the same cache states as the serial one, so both see the same hits and misses
+        store2 = TieredStore(host, args.cache_slots, dev)
+        cl2 = [store2.layer(l, dls[l].router, dls[l].shared) for l in range(NLc)]
         log("tiered store: %d layers in pinned host memory (%.2f GB), %d HBM slots per layer, built in %.1f s"
             % (NLc, host.buf.numel() / 1e9, args.cache_slots, time.time() - t0))
         ws1 = torch.empty(q.moe_workspace_bytes(shape, 1), dtype=torch.uint8, device=dev)
@@ -563,48 +630,61 @@ def main():
         hc = torch.empty(1, d, dtype=torch.bfloat16, device=dev)
         zoff = [torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=l)).to(dev) for l in range(NLc)]
 
+        copy_stream = torch.cuda.Stream()
+
         def token(t, layers, offs, through_cache):
-            # one token through the NLc layers with the residual in place; the picks go to
-            # the host (a synchronising copy) when the experts come through the cache
+            # one token through the NLc layers with the residual in place. Through the cache
+            # the picks go to the host (a synchronising copy); "overlap" copies the misses on
+            # their own stream while the shared expert and the hits run (CachedLayer.decode)
             hc.copy_(torch.from_numpy(synth.make_x(shape, 1, seed=500 + t, dtype="bf16")).view(torch.bfloat16))
             for l in range(NLc):
-                q.moe_router_topk(shape, layers[l].c, hc, 1, offs[l], cid, cw, None, ws1)
                 if through_cache:
-                    layers[l].acquire(cid.cpu().numpy())
+                    layers[l].decode(hc, offs[l], cid, cw, ceo, cy, hc, ws1,
+                                     copy_stream if through_cache == "overlap" else None)
+                    continue
+                q.moe_router_topk(shape, layers[l].c, hc, 1, offs[l], cid, cw, None, ws1)
                 q.moe_expert_ffn_decode(shape, layers[l].c, hc, cid, ceo, ws1)
                 q.moe_combine(shape, layers[l].c, hc, 1, ceo, None, cw, cy, hc, ws1)
 
-        def timed(layers, offs, through_cache, n_tok, first):
+        def timed(layers, offs, through_cache, n_tok, first, st=store):
             for t in range(3):
                 token(first + t, layers, offs, through_cache)
             torch.cuda.synchronize()
-            h0, m0, b0 = store.stats()
+            h0, m0, b0 = st.stats()
             t0 = time.time()
             for t in range(n_tok):
                 token(first + 3 + t, layers, offs, through_cache)
             torch.cuda.synchronize()
             dt = (time.time() - t0) / n_tok
-            h1, m1, b1 = store.stats()
+            h1, m1, b1 = st.stats()
             hits, misses, nb = h1 - h0, m1 - m0, b1 - b0
             return dt, hits, misses, nb
 
-        cache = {"workload": "decode, batch 1, %d-layer stack, residual in place; split calls (router, routed "
-                             "experts, shared + combine) with the picks copied to the host after each router; %d HBM "
+        cache = {"workload": "decode, batch 1, %d-layer stack, residual in place; split calls with the picks "
+                             "copied to the host after each router, the misses copied on their own stream while the "
+                             "shared expert and the hits run (serially for comparison); %d HBM "
                              "expert slots per layer (LFU) in front of all %d x %d blobs in pinned host memory"
                              % (NLc, args.cache_slots, NLc, E),
                  "slots_per_layer": args.cache_slots, "layers": NLc}
         n_tok = args.cache_tokens
         for name, offs in (("uniform_router", [None] * NLc), ("zipf_router", zoff)):
-            dt_c, hits, misses, nb = timed(cl, offs, True, n_tok, 0 if name == "uniform_router" else 10000)
-            dt_r, _, _, _ = timed(dls, offs, False, n_tok, 0 if name == "uniform_router" else 10000)
+            first = 0 if name == "uniform_router" else 10000
+            # the same tokens through the two stores: serial, then overlapped
+            dt_s, hits_s, misses_s, nb_s = timed(cl, offs, "serial", n_tok, first)
+            dt_c, hits, misses, nb = timed(cl2, offs, "overlap", n_tok, first, store2)
+            dt_r, _, _, _ = timed(dls, offs, False, n_tok, first)
             rec = {"ms_per_token": dt_c * 1e3, "tokens_per_s": 1.0 / dt_c, "hit_rate": hits / max(1, hits + misses),
                    "misses_per_token_layer": misses / (n_tok * NLc), "bytes_per_token": nb / n_tok,
                    "host_to_hbm_GBps": nb / n_tok / dt_c / 1e9,
+                   "serial_ms_per_token": dt_s * 1e3, "serial_hit_rate": hits_s / max(1, hits_s + misses_s),
+                   "serial_bytes_per_token": nb_s / n_tok, "overlap_gain": dt_s / dt_c,
                    "resident_ms_per_token": dt_r * 1e3, "slowdown_vs_resident": dt_c / dt_r, "tokens": n_tok}
             cache[name] = rec
-            log("tiered decode (%s): %.2f ms/token (%.1f tok/s), hit rate %.3f, %.2f misses per token-layer, "
+            log("tiered decode (%s): %.2f ms/token (%.1f tok/s) with the misses copied beside the shared expert and "
+                "the hits (serial: %.2f ms/token, %.2fx), hit rate %.3f (serial %.3f), %.2f misses per token-layer, "
                 "%.1f MB/token from the host tier (%.1f GB/s), resident split path %.2f ms/token (%.2fx)"
-                % (name, rec["ms_per_token"], rec["tokens_per_s"], rec["hit_rate"], rec["misses_per_token_layer"],
+                % (name, rec["ms_per_token"], rec["tokens_per_s"], rec["serial_ms_per_token"], rec["overlap_gain"],
+                   rec["hit_rate"], rec["serial_hit_rate"], rec["misses_per_token_layer"],
                    rec["bytes_per_token"] / 1e6, rec["host_to_hbm_GBps"], rec["resident_ms_per_token"],
                    rec["slowdown_vs_resident"]))
         # prefill chunks of 128 rows through the same cache: the routed experts in passes of
@@ -660,6 +740,7 @@ def main():
             % (RPc, rec["ms_per_chunk"], rec["passes_per_chunk"], rec["hit_rate"], rec["bytes_per_chunk"] / 1e6,
                rec["host_to_hbm_GBps"], rec["resident_ms_per_chunk"], rec["slowdown_vs_resident"]))
         store.close()
+        store2.close()
 
     # ---------------------------------------------------------------- CPU baseline (the oracle)
     cpu = None

@@ -196,7 +196,11 @@ moe_status moe_group_by_expert(const moe_shape* shape, const int32_t* topk_idx, 
  * review, section "TurboFieldfareとは", quantisation summary). The pages name no
  * activation; GeGLU with tanh-GELU on the gate is the reading taken here.
  * topk_idx is device memory [top_k]; ids outside [0, n_experts) or slot entries
- * outside the pool set the device error word and give zero outputs.
+ * outside the pool set the device error word and give zero outputs. A slot whose
+ * expert's table entry is MOE_SLOT_SKIP is left out without a flag: its row of
+ * expert_out keeps its contents. Decode through an expert cache runs this call twice
+ * on disjoint slots: the picks already resident while the misses are copied in, then
+ * the misses (see moe_shared_expert_decode).
  */
 moe_status moe_expert_ffn_decode(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                                  const int32_t* topk_idx, float* expert_out, void* ws, size_t ws_bytes,
@@ -245,6 +249,27 @@ moe_status moe_expert_ffn_prefill_chunk(const moe_shape* shape, const moe_layer*
 moe_status moe_combine(const moe_shape* shape, const moe_layer* layer, const void* x, moe_dtype x_dtype,
                        int32_t rows, const float* expert_out, const int32_t* inv_perm, const float* topk_w,
                        float* y, uint16_t* residual_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine for ONE decode row (inv_perm NULL) in two calls, so that other work can
+ * run between the shared expert and the combine. The pages run the shared-expert
+ * branch while the reads of the routed experts that missed the cache complete
+ * (blog-mushroom article, section "Why 26B Fits in 2 GB", per-token flow): here
+ * moe_shared_expert_decode goes first on the compute stream, the copies of the misses
+ * on another, and moe_combine_decode after the routed experts.
+ *   moe_shared_expert_decode: the shared expert of x (bf16 or fp32 [d_model]) into the
+ *     workspace; nothing else is written.
+ *   moe_combine_decode: y [d_model] = S(x) + sum_j topk_w[j] * expert_out[j] and the
+ *     residual store, as moe_combine; expert_out [top_k][d_model] unweighted.
+ * The pair gives y and residual bit-identical to moe_combine on the same inputs, if no
+ * call between them on the same workspace runs a shared expert or a whole-layer call
+ * (the routed-expert calls do not touch the shared expert's part of the workspace).
+ * Errors: as moe_combine; moe_combine_decode takes no layer and no x.
+ */
+moe_status moe_shared_expert_decode(const moe_shape* shape, const moe_layer* layer, const void* x,
+                                    moe_dtype x_dtype, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_combine_decode(const moe_shape* shape, const float* expert_out, const float* topk_w, float* y,
+                              uint16_t* residual_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Whole block for one decode row, fused: router + top-k + routed experts +
@@ -369,6 +394,41 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t slots, 
  */
 moe_status moe_cache_acquire(moe_expert_cache* cache, int32_t layer, const int32_t* idx_host, int32_t n,
                              int32_t* slot_host, int32_t* n_misses, void* stream);
+
+/*
+ * One decode row of `layer` through the cache, on `stream` (the pages' per-token flow:
+ * blog-mushroom article, section "Why 26B Fits in 2 GB"): the router; its picks read
+ * back to the host (the call waits for `stream` there); the cache makes them resident
+ * (moe_cache_acquire); the routed experts, the shared expert and the combine, with
+ * y and the residual store as moe_combine gives them on a resident pool. With
+ * copy_stream non-NULL the misses are copied on copy_stream, which first waits for the
+ * work already on `stream`, while `stream` runs the shared expert
+ * (moe_shared_expert_decode) and the picks that hit (moe_expert_ffn_decode over a table
+ * that skips the misses); `stream` then waits for the copies, runs the misses and the
+ * combine (moe_combine_decode). With copy_stream NULL, or when every pick is resident,
+ * the copies (if any) go first on `stream`, then moe_expert_ffn_decode and moe_combine.
+ *   router_blob, shared_blob  the layer's resident router and shared-expert blobs
+ *   x, x_dtype, logit_offset, topk_idx, topk_w, expert_out, y, residual_bf16  as
+ *                 moe_layer_decode (the routed experts come from the cache's slots)
+ *   pass_tables   device [2][n_experts] uint32 the call writes (NULL allowed without
+ *                 copy_stream); ws: moe_workspace_bytes(shape, 1)
+ * Errors: MOE_ERR_INVALID_ARG for a policy-only cache, a layer out of range, a shape
+ * whose n_experts differs from the cache's, top_k above the slots, blobs larger than
+ * the cache's stride, or copy_stream without pass_tables; the errors of the calls it
+ * makes (it stops at the first).
+ */
+moe_status moe_cache_decode(moe_expert_cache* cache, int32_t layer, const moe_shape* shape,
+                            const uint8_t* router_blob, const uint8_t* shared_blob, const void* x, moe_dtype x_dtype,
+                            const float* logit_offset, int32_t* topk_idx, float* topk_w, float* expert_out,
+                            float* y, uint16_t* residual_bf16, uint32_t* pass_tables, void* ws, size_t ws_bytes,
+                            void* stream, void* copy_stream);
+
+/* The slot of each expert idx_host[0..n) of `layer` as the cache stands (-1: not
+ * resident), without counting a request or changing anything; host-side only. A
+ * following moe_cache_acquire naming these experts keeps every resident one in its
+ * slot, so this tells the caller which picks hit before their misses are copied. */
+moe_status moe_cache_lookup(const moe_expert_cache* cache, int32_t layer, const int32_t* idx_host, int32_t n,
+                            int32_t* slot_host);
 
 /* Totals since creation: requests that hit, requests that missed, bytes copied. */
 moe_status moe_cache_stats(const moe_expert_cache* cache, uint64_t* hits, uint64_t* misses, uint64_t* bytes_copied);

@@ -97,6 +97,8 @@ def lib() -> C.CDLL:
             "moe_expert_ffn_decode": (st, [S, Ly, _P, st, _P, _P, _P, C.c_size_t, _P]),
             "moe_expert_ffn_prefill_chunk": (st, [S, Ly, _P, st, i32, _P, _P, _P, _P, C.c_size_t, _P]),
             "moe_combine": (st, [S, Ly, _P, st, i32, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+            "moe_shared_expert_decode": (st, [S, Ly, _P, st, _P, C.c_size_t, _P]),
+            "moe_combine_decode": (st, [S, _P, _P, _P, _P, _P, C.c_size_t, _P]),
             "moe_layer_decode": (st, [S, Ly, _P, st, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
             "moe_layer_decode_noalloc": (st, [S, Ly, _P, st, _P, _P, _P, _P, _P, _P, _P]),
             "moe_stack_decode": (st, [S, Ly, i32, _P, C.POINTER(_P), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
@@ -106,6 +108,9 @@ def lib() -> C.CDLL:
             "moe_check_device_error": (st, [_P, C.POINTER(C.c_uint32)]),
             "moe_cache_create": (st, [i32, i32, i32, u64, _P, _P, _P, C.POINTER(_P)]),
             "moe_cache_acquire": (st, [_P, i32, _P, i32, _P, _P, _P]),
+            "moe_cache_lookup": (st, [_P, i32, _P, i32, _P]),
+            "moe_cache_decode": (st, [_P, i32, S, _P, _P, _P, st, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P,
+                                      _P]),
             "moe_cache_stats": (st, [_P, C.POINTER(u64), C.POINTER(u64), C.POINTER(u64)]),
             "moe_cache_destroy": (st, [_P]),
         }
@@ -243,6 +248,18 @@ def moe_combine(shape, layer: moe_layer, x, rows: int, expert_out, inv_perm, top
                              _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_combine")
 
 
+def moe_shared_expert_decode(shape, layer: moe_layer, x, ws, stream=None) -> None:
+    _check(lib().moe_shared_expert_decode(C.byref(as_shape(shape)), C.byref(layer), _dptr(x), _dtype_code(x),
+                                          _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_shared_expert_decode")
+
+
+def moe_combine_decode(shape, expert_out, topk_w, y, residual, ws, stream=None) -> None:
+    _check(lib().moe_combine_decode(C.byref(as_shape(shape)), _dptr(expert_out), _dptr(topk_w), _dptr(y),
+                                    _dptr(residual), _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_combine_decode")
+
+
 def moe_layer_decode(shape, layer: moe_layer, x, logit_offset, topk_idx, topk_w, expert_out, y, residual, ws,
                      stream=None) -> None:
     _check(lib().moe_layer_decode(C.byref(as_shape(shape)), C.byref(layer), _dptr(x), _dtype_code(x),
@@ -317,6 +334,27 @@ def moe_cache_acquire(cache: int, layer: int, idx, slots=None, stream=None) -> i
                                    C.byref(miss), _stream(stream) if stream is not None or _cuda_ok() else None),
            "moe_cache_acquire")
     return miss.value
+
+
+def moe_cache_lookup(cache: int, layer: int, idx):
+    """The slots of the experts idx (host int32 array) as the cache stands, -1 where not
+    resident (nothing is counted or changed)."""
+    import numpy as np
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    slots = np.empty(idx.size, dtype=np.int32)
+    _check(lib().moe_cache_lookup(cache, layer, _hptr(idx), idx.size, _hptr(slots)), "moe_cache_lookup")
+    return slots
+
+
+def moe_cache_decode(cache: int, layer: int, shape, router_blob, shared_blob, x, logit_offset, topk_idx, topk_w,
+                     expert_out, y, residual, pass_tables, ws, stream=None, copy_stream=None) -> None:
+    """One decode row of `layer` through the cache (see moe.h); copy_stream: a torch
+    stream for the misses' copies (overlapped), or None (serial)."""
+    _check(lib().moe_cache_decode(cache, layer, C.byref(as_shape(shape)), _dptr(router_blob), _dptr(shared_blob),
+                                  _dptr(x), _dtype_code(x), _dptr(logit_offset), _dptr(topk_idx), _dptr(topk_w),
+                                  _dptr(expert_out), _dptr(y), _dptr(residual), _dptr(pass_tables), _dptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream),
+                                  None if copy_stream is None else _stream(copy_stream)), "moe_cache_decode")
 
 
 def moe_cache_stats(cache: int):

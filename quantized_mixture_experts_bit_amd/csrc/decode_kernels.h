@@ -142,6 +142,7 @@ struct DecodeArgs {
   float* shared_part; // [Ps][d]
   uint32_t* dn_count; // [d/64]
   int combine_arrivals;  // 0: no combine
+  int skip_ok;           // routed only, no combine: MOE_SLOT_SKIP entries leave their slots out
   const float* topk_w;
   float* y;
   uint16_t* residual;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs A, const XT* _
     slot = u / per;
     u -= slot * per;
     F = A.f;
-    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot], A.n_experts);
+    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot], A.n_experts, A.skip_ok != 0);
   } else {
     u -= A.routed_units;
     slot = A.top_k;
@@ -227,6 +228,27 @@ __global__ __launch_bounds__(256) void k_decode_gateup(DecodeArgs A, const XT* _
   }
 }
 
+// y[n] = the shared expert's parts summed in order, then + w_k E_k[n] in pick order;
+// residual[n] <- bf16(residual[n] + y[n]) when there is a residual
+__device__ __forceinline__ void combine_row(const DecodeArgs& A, int n) {
+  float sp[8], ev[16];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) sp[p] = p < A.Ps ? ld_agent(&A.shared_part[(size_t)p * A.d + n]) : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) ev[k] = k < A.top_k ? ld_agent(&A.expert_out[(size_t)k * A.d + n]) : 0.0f;
+  float yv = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) yv += sp[p];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < A.top_k) yv = fmaf(A.topk_w[k], ev[k], yv);
+  A.y[n] = yv;
+  if (A.residual) {
+    const float t = bf16_to_f32(A.residual[n]) + yv;
+    A.residual[n] = (uint16_t)f32_to_bf16_bits(t);
+  }
+}
+
 // down GEMVs (+ combine). Routed workgroup = (slot, 64-row block of d_model), all
 // of d_ff; shared workgroup = (64-row block, part of d_ff_shared).
 template <int GW>
@@ -239,13 +261,16 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs A) {
   int u = blockIdx.x;
   int slot, F, g0, g1, part = 0, nb;
   const uint8_t* blob;
+  bool skipped = false;  // a routed slot left out on purpose: its expert_out row is not written
   if (u < A.routed_units) {
     slot = u / NBd;
     nb = u % NBd;
     F = A.f;
     g0 = 0;
     g1 = F / kGroup;
-    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, A.topk_idx[slot], A.n_experts);
+    const int e = A.topk_idx[slot];
+    blob = expert_blob(A.pool, A.stride, A.n_blobs, A.slot_table, e, A.n_experts, A.skip_ok != 0);
+    skipped = A.skip_ok && !blob && e >= 0 && e < A.n_experts && A.slot_table[e] == kSlotSkip;
   } else {
     u -= A.routed_units;
     slot = A.top_k;
@@ -269,7 +294,7 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs A) {
   if (wave == 0) {
     float* dst = slot < A.top_k ? &A.expert_out[(size_t)slot * A.d + n] : &A.shared_part[(size_t)part * A.d + n];
     if (A.combine_arrivals == 0) {
-      *dst = r;
+      if (!skipped) *dst = r;
     } else {
       st_agent(dst, r);
       wait_mem();
@@ -280,24 +305,16 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs A) {
   __syncthreads();
   if (!last) return;
   if (wave == 0) {
-    float sp[8], ev[16];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) sp[p] = p < A.Ps ? ld_agent(&A.shared_part[(size_t)p * A.d + n]) : 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) ev[k] = k < A.top_k ? ld_agent(&A.expert_out[(size_t)k * A.d + n]) : 0.0f;
-    float yv = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) yv += sp[p];
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k < A.top_k) yv = fmaf(A.topk_w[k], ev[k], yv);
-    A.y[n] = yv;
-    if (A.residual) {
-      const float t = bf16_to_f32(A.residual[n]) + yv;
-      A.residual[n] = (uint16_t)f32_to_bf16_bits(t);
-    }
+    combine_row(A, n);
     if (lane == 0) A.dn_count[nb] = 0u;
   }
+}
+
+// The combine alone, after the shared expert's down parts (k_decode_down with the shared
+// expert and no combine) and the routed outputs are in memory: one thread per output.
+__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs A) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n < A.d) combine_row(A, n);
 }
 
 }  // namespace qmoe

@@ -41,6 +41,10 @@ struct moe_expert_cache {
   uint32_t* table_stage = nullptr;     // [L][E] pinned host copy of the slot tables
   std::vector<hipEvent_t> staged;      // [L] the last table copy of each layer
   std::vector<bool> staged_live;
+  // moe_cache_decode: the picks read back, the pass tables' staging, the stream joins
+  int32_t* pick_stage = nullptr;       // [16] pinned
+  uint32_t* pass_stage = nullptr;      // [L][2][E] pinned
+  hipEvent_t ev_main = nullptr, ev_copy = nullptr;
   uint64_t hits = 0, misses = 0, bytes = 0;
 };
 
@@ -52,7 +56,11 @@ void release(moe_expert_cache* c) {
   if (!c) return;
   for (size_t l = 0; l < c->staged.size(); ++l)
     if (c->staged_live[l]) (void)hipEventDestroy(c->staged[l]);
+  if (c->ev_main) (void)hipEventDestroy(c->ev_main);
+  if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
   if (c->table_stage) (void)hipHostFree(c->table_stage);
+  if (c->pick_stage) (void)hipHostFree(c->pick_stage);
+  if (c->pass_stage) (void)hipHostFree(c->pass_stage);
   delete c;
 }
 
@@ -94,6 +102,13 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t slots, 
       return MOE_ERR_HIP;
     }
     for (size_t i = 0; i < LE; ++i) c->table_stage[i] = (uint32_t)slots;
+    if (hipHostMalloc((void**)&c->pick_stage, 16 * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void**)&c->pass_stage, 2 * LE * sizeof(uint32_t), hipHostMallocDefault) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_main, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming) != hipSuccess) {
+      release(c);
+      return MOE_ERR_HIP;
+    }
     for (int32_t l = 0; l < n_layers; ++l) {
       if (hipEventCreateWithFlags(&c->staged[l], hipEventDisableTiming) != hipSuccess) {
         release(c);
@@ -133,6 +148,7 @@ moe_status moe_cache_acquire(moe_expert_cache* c, int32_t layer, const int32_t* 
   }
   int32_t miss = 0;
   bool table_changed = false;
+
   for (int32_t i = 0; i < n; ++i) {
     const int32_t e = idx_host[i];
     int32_t s = slot_of[e];
@@ -185,6 +201,85 @@ moe_status moe_cache_acquire(moe_expert_cache* c, int32_t layer, const int32_t* 
       return MOE_ERR_HIP;
   }
   if (n_misses) *n_misses = miss;
+  return MOE_OK;
+}
+
+moe_status moe_cache_decode(moe_expert_cache* c, int32_t layer, const moe_shape* shape, const uint8_t* router_blob,
+                            const uint8_t* shared_blob, const void* x, moe_dtype x_dtype, const float* logit_offset,
+                            int32_t* topk_idx, float* topk_w, float* expert_out, float* y, uint16_t* residual_bf16,
+                            uint32_t* pass_tables, void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
+  if (!c || c->host_only || !shape || layer < 0 || layer >= c->L) return MOE_ERR_INVALID_ARG;
+  if (shape->n_experts != c->E || shape->top_k > c->S || shape->top_k > 16 || shape->top_k < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (c->stride < moe_expert_blob_bytes(shape)) return MOE_ERR_INVALID_ARG;
+  if (copy_stream && !pass_tables) return MOE_ERR_INVALID_ARG;
+  const int32_t E = c->E, S = c->S, k = shape->top_k;
+  hipStream_t st = (hipStream_t)stream, cst = (hipStream_t)copy_stream;
+  // the layer as the kernels see it: its slots as the pool, its slot table
+  const moe_layer view{c->dev_slots + (size_t)layer * S * c->stride, c->stride, (uint64_t)S,
+                       c->dev_tables + (size_t)layer * E, router_blob, shared_blob};
+  moe_status r = moe_router_topk(shape, &view, x, x_dtype, 1, logit_offset, topk_idx, topk_w, nullptr, ws, ws_bytes,
+                                 stream);
+  if (r != MOE_OK) return r;
+  // the host needs the picks
+  if (hipMemcpyAsync(c->pick_stage, topk_idx, k * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return MOE_ERR_HIP;
+  const int32_t* picks = c->pick_stage;
+  int32_t before[16], slots[16];
+  if ((r = moe_cache_lookup(c, layer, picks, k, before)) != MOE_OK) return r;
+  const bool all_hit = std::all_of(before, before + k, [](int32_t v) { return v >= 0; });
+  if (!cst || all_hit) {
+    // serial (or nothing to copy): the copies, then the routed experts, the shared expert
+    // and the combine
+    if ((r = moe_cache_acquire(c, layer, picks, k, nullptr, nullptr, stream)) != MOE_OK) return r;
+    if ((r = moe_expert_ffn_decode(shape, &view, x, x_dtype, topk_idx, expert_out, ws, ws_bytes, stream)) != MOE_OK)
+      return r;
+    return moe_combine(shape, &view, x, x_dtype, 1, expert_out, nullptr, topk_w, y, residual_bf16, ws, ws_bytes,
+                       stream);
+  }
+  // overlapped: the picks resident now (`before`) keep their slots through the acquire.
+  // An evicted slot is overwritten only after the work already on the compute stream
+  if (hipEventRecord(c->ev_main, st) != hipSuccess || hipStreamWaitEvent(cst, c->ev_main, 0) != hipSuccess)
+    return MOE_ERR_HIP;
+  if ((r = moe_cache_acquire(c, layer, picks, k, slots, nullptr, copy_stream)) != MOE_OK) return r;
+  if (hipEventRecord(c->ev_copy, cst) != hipSuccess) return MOE_ERR_HIP;
+  // the shared expert while the misses come in
+  if ((r = moe_shared_expert_decode(shape, &view, x, x_dtype, ws, ws_bytes, stream)) != MOE_OK) return r;
+  // tables of the two passes: the picks that hit, then those that missed; MOE_SLOT_SKIP elsewhere
+  uint32_t* stage = c->pass_stage + (size_t)layer * 2 * E;
+  bool any_hit = false, any_miss = false;
+  for (int32_t i = 0; i < 2 * E; ++i) stage[i] = MOE_SLOT_SKIP;
+  for (int32_t i = 0; i < k; ++i) {
+    const bool hit = before[i] >= 0;
+    stage[(hit ? 0 : E) + picks[i]] = (uint32_t)slots[i];
+    any_hit |= hit;
+    any_miss |= !hit;
+  }
+  if (hipMemcpyAsync(pass_tables, stage, 2 * (size_t)E * sizeof(uint32_t), hipMemcpyHostToDevice, st) != hipSuccess)
+    return MOE_ERR_HIP;
+  moe_layer pass = view;
+  if (any_hit) {
+    pass.slot_table = pass_tables;
+    if ((r = moe_expert_ffn_decode(shape, &pass, x, x_dtype, topk_idx, expert_out, ws, ws_bytes, stream)) != MOE_OK)
+      return r;
+  }
+  if (hipStreamWaitEvent(st, c->ev_copy, 0) != hipSuccess) return MOE_ERR_HIP;
+  if (any_miss) {
+    pass.slot_table = pass_tables + E;
+    if ((r = moe_expert_ffn_decode(shape, &pass, x, x_dtype, topk_idx, expert_out, ws, ws_bytes, stream)) != MOE_OK)
+      return r;
+  }
+  return moe_combine_decode(shape, expert_out, topk_w, y, residual_bf16, ws, ws_bytes, stream);
+}
+
+moe_status moe_cache_lookup(const moe_expert_cache* c, int32_t layer, const int32_t* idx_host, int32_t n,
+                            int32_t* slot_host) {
+  if (!c || !idx_host || !slot_host || layer < 0 || layer >= c->L || n < 0) return MOE_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (idx_host[i] < 0 || idx_host[i] >= c->E) return MOE_ERR_INVALID_ARG;
+  const int32_t* slot_of = c->slot_of.data() + (size_t)layer * c->E;
+  for (int32_t i = 0; i < n; ++i) slot_host[i] = slot_of[idx_host[i]];
   return MOE_OK;
 }
 

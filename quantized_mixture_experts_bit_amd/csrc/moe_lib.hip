@@ -164,12 +164,14 @@ DecodeArgs decode_args(const moe_shape* s, const moe_layer* L, const int32_t* id
   const DecodeCfg dc = decode_cfg(s);
   DecodeArgs A;
   memset(&A, 0, sizeof A);
-  A.pool = L->pool;
-  A.stride = L->blob_stride;
-  A.n_blobs = L->n_blobs;
-  A.slot_table = L->slot_table;
+  if (L) {  // null for the combine alone
+    A.pool = L->pool;
+    A.stride = L->blob_stride;
+    A.n_blobs = L->n_blobs;
+    A.slot_table = L->slot_table;
+    A.shared_blob = L->shared_blob;
+  }
   A.topk_idx = idx;
-  A.shared_blob = L->shared_blob;
   A.d = s->d_model;
   A.f = s->d_ff;
   A.fs = s->d_ff_shared;
@@ -544,11 +546,40 @@ moe_status moe_expert_ffn_decode(const moe_shape* s, const moe_layer* L, const v
   if (!idx || !expert_out) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = (hipStream_t)stream;
   DecodeArgs A = decode_args(s, L, idx, ws, ws_layout(s, 1), expert_out, nullptr, nullptr, nullptr);
+  A.skip_ok = 1;
   if (dt == MOE_BF16)
     launch_decode_gateup(A, (const uint16_t*)x, true, false, hs);
   else
     launch_decode_gateup(A, (const float*)x, true, false, hs);
   launch_decode_down(A, true, false, false, hs);
+  return launched();
+}
+
+moe_status moe_shared_expert_decode(const moe_shape* s, const moe_layer* L, const void* x, moe_dtype dt, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  moe_status st = check_common(s, x, dt, 1, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if ((st = check_layer(s, L, false, false, true)) != MOE_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  DecodeArgs A = decode_args(s, L, nullptr, ws, ws_layout(s, 1), nullptr, nullptr, nullptr, nullptr);
+  if (dt == MOE_BF16)
+    launch_decode_gateup(A, (const uint16_t*)x, false, true, hs);
+  else
+    launch_decode_gateup(A, (const float*)x, false, true, hs);
+  launch_decode_down(A, false, true, false, hs);  // the down parts stay in the workspace
+  return launched();
+}
+
+moe_status moe_combine_decode(const moe_shape* s, const float* expert_out, const float* topk_w, float* y,
+                              uint16_t* residual, void* ws, size_t ws_bytes, void* stream) {
+  if (!shape_ok(s)) return s ? MOE_ERR_UNSUPPORTED_SHAPE : MOE_ERR_INVALID_ARG;
+  if (!ws || ((uintptr_t)ws & 255u)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ws_layout(s, 1).total) return MOE_ERR_WORKSPACE;
+  if (!expert_out || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(expert_out) || !aligned16(y) || ((uintptr_t)residual & 7u)) return MOE_ERR_INVALID_ARG;
+  DecodeArgs A = decode_args(s, nullptr, nullptr, ws, ws_layout(s, 1), const_cast<float*>(expert_out), topk_w, y,
+                             residual);
+  k_decode_combine<<<cdiv(s->d_model, 256), 256, 0, (hipStream_t)stream>>>(A);
   return launched();
 }
 

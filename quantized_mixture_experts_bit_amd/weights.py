@@ -19,10 +19,10 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MOE_SLOT_SKIP, as_shape, moe_cache_acquire, moe_cache_create, moe_cache_destroy, moe_cache_stats,
-               moe_combine, moe_expert_blob_bytes, moe_expert_ffn_prefill_chunk, moe_group_by_expert, moe_layer,
-               moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4, moe_pack_matrix8, moe_router_blob_bytes,
-               moe_router_topk, moe_shared_blob_bytes)
+from . import (MOE_SLOT_SKIP, as_shape, moe_cache_acquire, moe_cache_create, moe_cache_decode, moe_cache_destroy,
+               moe_cache_stats, moe_combine, moe_expert_blob_bytes, moe_expert_ffn_prefill_chunk, moe_group_by_expert,
+               moe_layer, moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4, moe_pack_matrix8,
+               moe_router_blob_bytes, moe_router_topk, moe_shared_blob_bytes)
 
 BLOB_ALIGN = 4096  # blob stride granularity (a page)
 
@@ -152,10 +152,21 @@ class CachedLayer:
         self.pass_table = torch.empty(store.shape.n_experts, dtype=torch.int32, device=store.tables.device)
         self.pass_view = moe_layer(store.dev_slots.data_ptr() + l * S * st, st, S, self.pass_table.data_ptr(),
                                    router.data_ptr(), shared.data_ptr())
+        # decode: the tables of the passes over the picks that hit and those that missed
+        self.dec_tables = torch.empty(2, store.shape.n_experts, dtype=torch.int32, device=store.tables.device)
 
     def acquire(self, idx, slots=None, stream=None) -> int:
         """Makes the experts idx (host int32 array) resident; returns the misses."""
         return moe_cache_acquire(self.store.handle, self.l, idx, slots, stream)
+
+    def decode(self, x, logit_offset, topk_idx, topk_w, expert_out, y, residual, ws, copy_stream=None) -> None:
+        """One decode row through the cache on the current stream (moe_cache_decode): the
+        router, its picks to the host, the cache makes them resident; with copy_stream the
+        misses are copied on it while the shared expert and the picks that hit run (the
+        pages' per-token flow), without it the copies go first. y and the residual are
+        bit-identical to the split calls on a resident pool."""
+        moe_cache_decode(self.store.handle, self.l, self.store.shape, self.router, self.shared, x, logit_offset,
+                         topk_idx, topk_w, expert_out, y, residual, self.dec_tables, ws, None, copy_stream)
 
     def prefill(self, x, rows: int, logit_offset, topk_idx, topk_w, count, offset, perm, inv_perm, expert_out,
                 y, residual, ws):

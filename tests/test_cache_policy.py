@@ -54,8 +54,15 @@ def run_both(n_layers, E, S, requests):
         for layer, idx in requests:
             idx = np.asarray(idx, dtype=np.int32)
             slots = np.empty(idx.size, dtype=np.int32)
+            # lookup: the model's residency before the request, nothing counted
+            before = q.moe_cache_lookup(h, layer, idx)
+            assert before.tolist() == [m.slot_of[layer].get(int(e), -1) for e in idx]
+            assert q.moe_cache_stats(h)[:2] == (m.hits, m.misses)
             miss = q.moe_cache_acquire(h, layer, idx, slots)
             want, want_miss = m.acquire(layer, [int(v) for v in idx])
+            # a resident expert keeps its slot through the request that names it
+            assert all(b < 0 or b == s for b, s in zip(before.tolist(), want))
+            assert miss == int((before < 0).sum())
             assert slots.tolist() == want, (layer, idx.tolist())
             assert miss == want_miss
         hits, misses, nbytes = q.moe_cache_stats(h)
@@ -107,6 +114,17 @@ def test_random_streams_match_the_model(n_layers, E, S, k, skew):
         assert m.hits > m.misses  # skewed routing reuses experts when the cache holds two requests
 
 
+def test_lookup_rejects_bad_arguments():
+    h = q.moe_cache_create(2, 64, 4)
+    try:
+        for layer, idx in ((2, [0]), (-1, [0]), (0, [64]), (0, [-1])):
+            with pytest.raises(q.MoeError):
+                q.moe_cache_lookup(h, layer, np.asarray(idx, dtype=np.int32))
+        assert q.moe_cache_lookup(h, 0, np.zeros(0, dtype=np.int32)).size == 0
+    finally:
+        q.moe_cache_destroy(h)
+
+
 def test_invalid_requests_are_rejected():
     h = q.moe_cache_create(2, 64, 4)
     try:
@@ -120,3 +138,16 @@ def test_invalid_requests_are_rejected():
     for args in [(0, 64, 4), (1, 64, 0), (1, 64, 65), (1, 0, 1), (1, 300, 4)]:
         with pytest.raises(q.MoeError):
             q.moe_cache_create(*args)
+
+
+def test_cache_decode_needs_a_device_cache():
+    import ctypes as C
+    h = q.moe_cache_create(1, 64, 8)  # policy only: no device side
+    try:
+        s = q.MoeShape(2816, 704, 2112, n_experts=64)
+        args = [0x10000, 0x20000, 0x50000, q.MOE_BF16, None, 0x60000, 0x70000, 0x80000, 0x90000, None, 0xA0000,
+                0xB0000, 1 << 30, None, None]
+        assert q.lib().moe_cache_decode(h, 0, C.byref(s), *args) == q.MOE_ERR_INVALID_ARG
+        assert q.lib().moe_cache_decode(None, 0, C.byref(s), *args) == q.MOE_ERR_INVALID_ARG
+    finally:
+        q.moe_cache_destroy(h)

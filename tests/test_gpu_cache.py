@@ -1,8 +1,10 @@
 """Decode through the tiered expert store (HBM slots per layer in front of a pinned host
 pool, moe_cache_*) gives the same bits as decode over the all-resident pool: the same
 kernels run on the same bytes, reached through the cache's slot tables. Checked over a
-stream of tokens that hits, misses and evicts. The cached outputs are also checked
-against the fp64 oracle (picks, every unweighted expert output and y)."""
+stream of tokens that hits, misses and evicts, in both decode flows (the misses copied
+first, or on their own stream while the shared expert and the hits run). The cached
+outputs are also checked against the fp64 oracle (picks, every unweighted expert output
+and y)."""
 import numpy as np
 import pytest
 import torch
@@ -16,17 +18,22 @@ q = pytest.importorskip("quantized_mixture_experts_bit_amd")
 from quantized_mixture_experts_bit_amd.weights import HostExpertPool, TieredStore, upload_layers  # noqa: E402
 
 
-def decode_split(shape, layer_c, x, off, ws, cached=None):
-    """Router, (cache acquire), routed experts, shared + combine: the split calls."""
+def decode_split(shape, layer_c, x, off, ws, cached=None, copy_stream=None):
+    """Router, routed experts, shared + combine: the split calls on a resident pool, or
+    through the cache (CachedLayer.decode: serial, or overlapped with copy_stream)."""
     k, d = shape.top_k, shape.d_model
     idx, w = empty_i32(k), empty_f32(k)
     eo, y = empty_f32(k, d), empty_f32(d)
-    q.moe_router_topk(shape, layer_c, x, 1, off, idx, w, None, ws)
+    eo.fill_(float("nan"))  # every row must be written
     miss = None
     if cached is not None:
-        miss = cached.acquire(idx.cpu().numpy())  # the host needs the picks: a synchronising copy
-    q.moe_expert_ffn_decode(shape, layer_c, x, idx, eo, ws)
-    q.moe_combine(shape, layer_c, x, 1, eo, None, w, y, None, ws)
+        m0 = cached.store.stats()[1]
+        cached.decode(x, off, idx, w, eo, y, None, ws, copy_stream)
+        miss = cached.store.stats()[1] - m0
+    else:
+        q.moe_router_topk(shape, layer_c, x, 1, off, idx, w, None, ws)
+        q.moe_expert_ffn_decode(shape, layer_c, x, idx, eo, ws)
+        q.moe_combine(shape, layer_c, x, 1, eo, None, w, y, None, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), eo.cpu().numpy(), y.cpu().numpy(), miss
 
@@ -49,12 +56,15 @@ def test_cached_decode_matches_resident(shape, slots, zipf):
         ws = workspace(shape, 1)
         total_miss = 0
         olayers = [O.OracleLayer(L) for L in layers]
+        copy_stream = torch.cuda.Stream()
         for t in range(tokens):
             for l in range(n_layers):
                 x_np = synth.make_x(shape, 1, seed=100 + t, stream=l, dtype="bf16")
                 x = to_dev_x(x_np)
                 i0, e0, y0, _ = decode_split(shape, resident[l].c, x, offs[l], ws)
-                i1, e1, y1, miss = decode_split(shape, cached[l].c, x, offs[l], ws, cached[l])
+                # odd tokens: the misses copied on their own stream beside the shared expert and the hits
+                i1, e1, y1, miss = decode_split(shape, None, x, offs[l], ws, cached[l],
+                                                copy_stream if t % 2 else None)
                 np.testing.assert_array_equal(i1, i0)
                 assert np.array_equal(e1.view(np.uint32), e0.view(np.uint32)), (t, l)
                 assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32)), (t, l)
@@ -138,3 +148,62 @@ def test_cached_prefill_matches_resident(rows, zipf):
         assert q.moe_check_device_error() == 0
     finally:
         store.close()
+
+
+def test_split_combine_matches_combine():
+    """moe_shared_expert_decode, then moe_combine_decode gives moe_combine's y and residual
+    bits, also with the routed experts run between the two."""
+    shape = synth.GEMMA4
+    k, d = shape.top_k, shape.d_model
+    (dl,) = upload_layers(shape, [synth.make_layer(shape, seed=9, layer=0)], device())
+    ws = workspace(shape, 1)
+    for seed in range(3):
+        x = to_dev_x(synth.make_x(shape, 1, seed=60 + seed, dtype="bf16"))
+        idx, w, eo = empty_i32(k), empty_f32(k), empty_f32(k, d)
+        q.moe_router_topk(shape, dl.c, x, 1, None, idx, w, None, ws)
+        q.moe_expert_ffn_decode(shape, dl.c, x, idx, eo, ws)
+        y0, y1 = empty_f32(d), empty_f32(d)
+        r0, r1 = x.clone(), x.clone()
+        q.moe_combine(shape, dl.c, x, 1, eo, None, w, y0, r0, ws)
+        q.moe_shared_expert_decode(shape, dl.c, x, ws)
+        q.moe_expert_ffn_decode(shape, dl.c, x, idx, eo, ws)  # between the two: same outputs again
+        q.moe_combine_decode(shape, eo, w, y1, r1, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), y0.view(torch.int32)), seed
+        assert torch.equal(r1.view(torch.int16), r0.view(torch.int16)), seed
+    assert q.moe_check_device_error() == 0
+
+
+def test_decode_experts_skip_entries():
+    """moe_expert_ffn_decode leaves the slots whose table entry is MOE_SLOT_SKIP alone (no
+    flag, rows untouched); two passes over complementary tables give one pass's bits."""
+    shape = synth.GEMMA4
+    k, d, E = shape.top_k, shape.d_model, shape.n_experts
+    (dl,) = upload_layers(shape, [synth.make_layer(shape, seed=9, layer=0)], device())
+    ws = workspace(shape, 1)
+    x = to_dev_x(synth.make_x(shape, 1, seed=77, dtype="bf16"))
+    idx, w = empty_i32(k), empty_f32(k)
+    q.moe_router_topk(shape, dl.c, x, 1, None, idx, w, None, ws)
+    full = empty_f32(k, d)
+    q.moe_expert_ffn_decode(shape, dl.c, x, idx, full, ws)
+    table = dl.slot_table.cpu().numpy().view(np.uint32)
+    picks = idx.cpu().numpy()
+    first = np.zeros(E, dtype=bool)
+    first[picks[::2]] = True  # even slots in the first pass, odd slots in the second
+    tabs = []
+    for part in (first, ~first):
+        t = np.full(E, q.MOE_SLOT_SKIP, dtype=np.uint32)
+        t[part] = table[part]
+        tabs.append(torch.from_numpy(t.view(np.int32)).to(device()))
+    views = [q.moe_layer(dl.c.pool, dl.c.blob_stride, dl.c.n_blobs, t.data_ptr(), dl.c.router_blob,
+                         dl.c.shared_blob) for t in tabs]
+    out = torch.full((k, d), float("nan"), device=device())
+    q.moe_expert_ffn_decode(shape, views[0], x, idx, out, ws)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isnan(o[1::2]).all()  # skipped slots untouched
+    assert np.array_equal(o[::2].view(np.uint32), full.cpu().numpy()[::2].view(np.uint32))
+    q.moe_expert_ffn_decode(shape, views[1], x, idx, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), full.view(torch.int32))
+    assert q.moe_check_device_error() == 0

@@ -171,10 +171,33 @@ def test_misaligned_combine_buffers_are_rejected():
         return lib.moe_layer_prefill(C.byref(s), L, 0x50000, q.MOE_BF16, 4, None, 0xB0000, 0x70000, 0xC0000,
                                      0xD0000, 0xE0000, 0xA0000, eo, y, res, 0x80000, 1 << 30, None)
 
-    for call in (combine, prefill):
+    def combine_decode(eo=0x60000, y=0x90000, res=None):
+        return lib.moe_combine_decode(C.byref(s), eo, 0x70000, y, res, 0x80000, 1 << 30, None)
+
+    for call in (combine, prefill, combine_decode):
         assert call(eo=0x60004) == q.MOE_ERR_INVALID_ARG
         assert call(y=0x90008) == q.MOE_ERR_INVALID_ARG
         assert call(res=0x50002) == q.MOE_ERR_INVALID_ARG
+
+
+def test_split_combine_arguments_are_rejected():
+    lib = q.lib()
+    s = q.MoeShape(2816, 704, 2112)
+    assert lib.moe_combine_decode(C.byref(s), None, 0x70000, 0x90000, None, 0x80000, 1 << 30, None) == \
+        q.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_decode(C.byref(s), 0x60000, 0x70000, 0x90000, None, 0x80010, 1 << 30, None) == \
+        q.MOE_ERR_INVALID_ARG  # workspace not 256-byte aligned
+    assert lib.moe_combine_decode(C.byref(s), 0x60000, 0x70000, 0x90000, None, 0x80000, 16, None) == \
+        q.MOE_ERR_WORKSPACE
+    assert lib.moe_combine_decode(C.byref(q.MoeShape(2816, 704, 2112, top_k=0)), 0x60000, 0x70000, 0x90000, None,
+                                  0x80000, 1 << 30, None) == q.MOE_ERR_UNSUPPORTED_SHAPE
+    assert lib.moe_shared_expert_decode(C.byref(s), None, 0x50000, q.MOE_BF16, 0x80000, 1 << 30, None) == \
+        q.MOE_ERR_INVALID_ARG
+    no_shared = q.moe_layer(0x10000, 3346432, 128, 0x20000, 0x30000, 0)
+    assert lib.moe_shared_expert_decode(C.byref(s), C.byref(no_shared), 0x50000, q.MOE_BF16, 0x80000, 1 << 30,
+                                        None) == q.MOE_ERR_INVALID_ARG
+    assert lib.moe_shared_expert_decode(C.byref(s), C.byref(_fake_layer()), 0x50004, q.MOE_BF16, 0x80000, 1 << 30,
+                                        None) == q.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():
