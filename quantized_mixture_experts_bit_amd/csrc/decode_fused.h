@@ -115,18 +115,21 @@ struct FusedSmem {
 };
 
 // Timeline build (QMOE_TIMELINE): thread 0 of each workgroup stamps the 100 MHz
-// real-time counter at the phase boundaries of its item into
-// g_timeline[layer][block][slot] (kStamps slots per block; the slot meanings per item
-// kind are listed at each QMOE_STAMP; F is the item's FusedArgs). The default build
-// compiles the stamps away.
+// real-time counter at the phase boundaries of its item into g_timeline[block][slot],
+// in a stacked decode g_timeline[layer][block][slot] (kStamps slots per block; the slot
+// meanings per item kind are listed at each QMOE_STAMP, which names the item's
+// FusedArgs F and the kStack of the function it is in). The default build compiles the
+// stamps away.
 constexpr int kStamps = 8;
 #ifdef QMOE_TIMELINE
 __device__ uint64_t* g_timeline = nullptr;
-#define QMOE_STAMP(slot)                                                                        \
-  do {                                                                                          \
-    if (threadIdx.x == 0 && g_timeline)                                                         \
-      g_timeline[((size_t)F.layer * gridDim.x + blockIdx.x) * kStamps + (slot)] =               \
-          __builtin_amdgcn_s_memrealtime();                                                     \
+#define QMOE_STAMP(slot)                                                                       \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && g_timeline) {                                                      \
+      size_t row_ = blockIdx.x;                                                                \
+      if constexpr (kStack) row_ += (size_t)F.layer * gridDim.x;                               \
+      g_timeline[row_ * kStamps + (slot)] = __builtin_amdgcn_s_memrealtime();                  \
+    }                                                                                          \
   } while (0)
 #else
 #define QMOE_STAMP(slot) \
@@ -345,6 +348,7 @@ __device__ __forceinline__ void load_logits(const FusedArgs& F, uint32_t tag, Fu
 // and a shift, independent of each other and summed in four chains. That is the true order wherever the truncated parts
 // differ; when two neighbours among ranks 0..top_k share theirs, the logits are read
 // in full and the ranking is redone on the whole keys (rank_topk). Ends with a barrier.
+template <bool kStack>
 __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
   const int tid = threadIdx.x, E = F.E, k = F.top_k;
   const uint64_t* lk = F.lg_tag + (size_t)(blockIdx.x % kLgCopies) * kLgStride + kLgKeys;
@@ -391,10 +395,11 @@ __device__ __forceinline__ void rank_logits(const FusedArgs& F, uint32_t tag, Fu
 
 // The blob of the expert picked for `slot` (nullptr and the error flag if its table
 // entry is outside the pool). slot_entry: thread t < E holds slot_table[t].
+template <bool kStack>
 __device__ __forceinline__ const uint8_t* routed_blob(const FusedArgs& F, int slot, uint32_t tag,
                                                       uint32_t slot_entry, FusedSmem& S) {
   if (threadIdx.x < F.E) S.slots[threadIdx.x] = slot_entry;
-  rank_logits(F, tag, S);
+  rank_logits<kStack>(F, tag, S);
   const uint32_t b = S.slots[S.sel_e[slot]];  // ranks are a permutation: sel_e is a valid id
   if ((uint64_t)b >= F.n_blobs) {
     if (threadIdx.x == 0) flag_device_error(1u);
@@ -562,7 +567,7 @@ __device__ __forceinline__ void fused_gateup(const FusedArgs& F, const XT* __res
   stage_x<XT, false, kStack>(x, F, tag, S);
   if (routed) {
     // the arrival goes after the weight loads: no wait on the ticket's path covers it
-    blob = routed_blob(F, slot, tag, slot_entry, S);
+    blob = routed_blob<kStack>(F, slot, tag, slot_entry, S);
     if (blob) load(blob);
     if (tid == 0) arrive_epoch<kStack>(F, epoch);
   }
@@ -723,7 +728,7 @@ __device__ __attribute__((noinline)) double exp_call(double v) { return exp(v); 
 template <bool kStack>
 __device__ __forceinline__ void pick_weights(const FusedArgs& F, uint32_t tag, FusedSmem& S) {
   const int tid = thread_index<kStack>(), lane = tid & 63, k = F.top_k;
-  rank_logits(F, tag, S);
+  rank_logits<kStack>(F, tag, S);
   load_logits(F, tag, S);  // the picked logits for the weights (long published by now)
   if (tid < 64) {
     double ex = 0.0;
@@ -803,7 +808,7 @@ __device__ __forceinline__ void fused_down(const FusedArgs& F, int u, int kind, 
   // a later layer of a stacked decode: the waits for the keys and for h start once this
   // layer's input is in (they would otherwise poll through the previous layer's tail)
   if (kStack && kind == 0 && F.x_in) wait_x_in(F, tag);
-  const uint8_t* blob = kind == 0 ? routed_blob(F, slot, tag, slot_entry, S) : F.shared_blob;
+  const uint8_t* blob = kind == 0 ? routed_blob<kStack>(F, slot, tag, slot_entry, S) : F.shared_blob;
   RowLoads<GW> w;
   const uint8_t* rowblock = blob ? blob + 2 * m4_bytes(Fd, F.d) + (uint64_t)ob * Gin * kTile4 : nullptr;
   const uint64_t* hsrc = F.h_tag + (blockIdx.x % kHCopies) * F.h_stride + (size_t)slot * F.fmax;
@@ -870,6 +875,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& F, const XT* __restr
 template <typename XT>
 __global__ __launch_bounds__(256, 4) void k_decode_fused(FusedArgs F, const XT* __restrict__ x) {
   __shared__ FusedSmem S;
+  constexpr bool kStack = false;
   QMOE_STAMP(0);  // every item: started
   const uint32_t epoch = read_epoch(F);
   if (blockIdx.x == gridDim.x - 1) return epoch_keeper(F, epoch);
@@ -983,6 +989,7 @@ __global__ __launch_bounds__(256, 4) void k_stack_decode(StackArgs A, const XT* 
   auto layers = [&](auto item) __attribute__((always_inline)) {
     for (int l = 0; l < A.n_layers; ++l) {
       const FusedArgs F = stack_layer_args(l);
+      constexpr bool kStack = true;
       QMOE_STAMP(0);  // every item: started (the layer)
       item(F, epoch + 1u + (uint32_t)l);
       __syncthreads();  // the next layer's item reuses the LDS
