@@ -56,6 +56,15 @@ def run_both(shape, n_layers, variant, zipf, dtype_seed=7):
     pytest.param(synth.TINY, 5, synth.LIVE_STACK, True, id="tiny-5layers-live-zipf"),
     pytest.param(synth.GEMMA4, 3, synth.Variant(router_scale_log2=-6), False, id="gemma4-3layers-soft"),
     pytest.param(BEYOND_FF, 3, synth.Variant(router_scale_log2=-6), True, id="dff832-3layers-layer-by-layer"),
+    # the most layers one launch takes, on the tiny shape
+    pytest.param(synth.TINY, 32, synth.LIVE_STACK, True, id="tiny-32layers-live-zipf"),
+    # 256 experts, top-16 (the rankers' other share split), and 64 experts
+    pytest.param(synth.MoeShape(512, 256, 512, n_experts=256, top_k=16), 3, synth.LIVE_STACK, True,
+                 id="e256-k16-3layers"),
+    pytest.param(synth.MoeShape(1024, 512, 1024, n_experts=64, top_k=4), 4, synth.LIVE_STACK, False,
+                 id="e64-k4-4layers"),
+    # more than one launch takes: layer by layer inside the call
+    pytest.param(synth.TINY, 33, synth.LIVE_STACK, False, id="tiny-33layers-layer-by-layer"),
 ])
 def test_stack_decode_matches_layer_calls(shape, n_layers, variant, zipf):
     canon, offs, ref, final, got, x_out = run_both(shape, n_layers, variant, zipf)
