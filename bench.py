@@ -621,6 +621,11 @@ def main():
         # the same cache states as the serial one, so both see the same hits and misses
         store2 = TieredStore(host, args.cache_slots, dev)
         cl2 = [store2.layer(l, dls[l].router, dls[l].shared) for l in range(NLc)]
+        # and two stores with the policy on the device (eager, and one HIP graph per token)
+        store3 = TieredStore(host, args.cache_slots, dev, device_policy=True)
+        cl3 = [store3.layer(l, dls[l].router, dls[l].shared) for l in range(NLc)]
+        store4 = TieredStore(host, args.cache_slots, dev, device_policy=True)
+        cl4 = [store4.layer(l, dls[l].router, dls[l].shared) for l in range(NLc)]
         log("tiered store: %d layers in pinned host memory (%.2f GB), %d HBM slots per layer, built in %.1f s"
             % (NLc, host.buf.numel() / 1e9, args.cache_slots, time.time() - t0))
         ws1 = torch.empty(q.moe_workspace_bytes(shape, 1), dtype=torch.uint8, device=dev)
@@ -637,6 +642,9 @@ def main():
             # the picks go to the host (a synchronising copy); "overlap" copies the misses on
             # their own stream while the shared expert and the hits run (CachedLayer.decode)
             hc.copy_(torch.from_numpy(synth.make_x(shape, 1, seed=500 + t, dtype="bf16")).view(torch.bfloat16))
+            if through_cache == "graph":
+                token_graph[offs_key(offs)].replay()
+                return
             for l in range(NLc):
                 if through_cache:
                     layers[l].decode(hc, offs[l], cid, cw, ceo, cy, hc, ws1,
@@ -645,6 +653,20 @@ def main():
                 q.moe_router_topk(shape, layers[l].c, hc, 1, offs[l], cid, cw, None, ws1)
                 q.moe_expert_ffn_decode(shape, layers[l].c, hc, cid, ceo, ws1)
                 q.moe_combine(shape, layers[l].c, hc, 1, ceo, None, cw, cy, hc, ws1)
+
+        token_graph = {}
+
+        def offs_key(offs):
+            return "zipf" if offs[0] is not None else "uniform"
+
+        def capture_token(layers, offs):
+            # one token's layers through a device-policy store, captured once (the capture
+            # runs nothing, so the store's history is untouched)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                for l in range(NLc):
+                    layers[l].decode(hc, offs[l], cid, cw, ceo, cy, hc, ws1)
+            token_graph[offs_key(offs)] = g
 
         def timed(layers, offs, through_cache, n_tok, first, st=store):
             for t in range(3):
@@ -662,7 +684,8 @@ def main():
 
         cache = {"workload": "decode, batch 1, %d-layer stack, residual in place; split calls with the picks "
                              "copied to the host after each router, the misses copied on their own stream while the "
-                             "shared expert and the hits run (serially for comparison); %d HBM "
+                             "shared expert and the hits run (serially for comparison), and with the policy on the "
+                             "device (no host round trip; eager, and one HIP graph per token); %d HBM "
                              "expert slots per layer (LFU) in front of all %d x %d blobs in pinned host memory"
                              % (NLc, args.cache_slots, NLc, E),
                  "slots_per_layer": args.cache_slots, "layers": NLc}
@@ -672,12 +695,19 @@ def main():
             # the same tokens through the two stores: serial, then overlapped
             dt_s, hits_s, misses_s, nb_s = timed(cl, offs, "serial", n_tok, first)
             dt_c, hits, misses, nb = timed(cl2, offs, "overlap", n_tok, first, store2)
+            dt_d, hits_d, misses_d, nb_d = timed(cl3, offs, "device", n_tok, first, store3)
+            capture_token(cl4, offs)
+            dt_g, hits_g, misses_g, nb_g = timed(cl4, offs, "graph", n_tok, first, store4)
             dt_r, _, _, _ = timed(dls, offs, False, n_tok, first)
             rec = {"ms_per_token": dt_c * 1e3, "tokens_per_s": 1.0 / dt_c, "hit_rate": hits / max(1, hits + misses),
                    "misses_per_token_layer": misses / (n_tok * NLc), "bytes_per_token": nb / n_tok,
                    "host_to_hbm_GBps": nb / n_tok / dt_c / 1e9,
                    "serial_ms_per_token": dt_s * 1e3, "serial_hit_rate": hits_s / max(1, hits_s + misses_s),
                    "serial_bytes_per_token": nb_s / n_tok, "overlap_gain": dt_s / dt_c,
+                   "device_policy_ms_per_token": dt_d * 1e3,
+                   "device_policy_hit_rate": hits_d / max(1, hits_d + misses_d),
+                   "device_policy_graph_ms_per_token": dt_g * 1e3,
+                   "device_policy_graph_hit_rate": hits_g / max(1, hits_g + misses_g),
                    "resident_ms_per_token": dt_r * 1e3, "slowdown_vs_resident": dt_c / dt_r, "tokens": n_tok}
             cache[name] = rec
             log("tiered decode (%s): %.2f ms/token (%.1f tok/s) with the misses copied beside the shared expert and "
@@ -687,6 +717,10 @@ def main():
                    rec["hit_rate"], rec["serial_hit_rate"], rec["misses_per_token_layer"],
                    rec["bytes_per_token"] / 1e6, rec["host_to_hbm_GBps"], rec["resident_ms_per_token"],
                    rec["slowdown_vs_resident"]))
+            log("tiered decode (%s), policy on the device: %.2f ms/token eager, %.2f ms/token as one HIP graph per "
+                "token (hit rates %.3f, %.3f)" % (name, rec["device_policy_ms_per_token"],
+                                                  rec["device_policy_graph_ms_per_token"],
+                                                  rec["device_policy_hit_rate"], rec["device_policy_graph_hit_rate"]))
         # prefill chunks of 128 rows through the same cache: the routed experts in passes of
         # at most `slots` experts (MOE_SLOT_SKIP for the others), against the same split
         # calls on the resident pool
@@ -741,6 +775,8 @@ def main():
                rec["host_to_hbm_GBps"], rec["resident_ms_per_chunk"], rec["slowdown_vs_resident"]))
         store.close()
         store2.close()
+        store3.close()
+        store4.close()
 
     # ---------------------------------------------------------------- CPU baseline (the oracle)
     cpu = None

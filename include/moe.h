@@ -423,6 +423,31 @@ moe_status moe_cache_decode(moe_expert_cache* cache, int32_t layer, const moe_sh
                             float* y, uint16_t* residual_bf16, uint32_t* pass_tables, void* ws, size_t ws_bytes,
                             void* stream, void* copy_stream);
 
+/*
+ * The same cache with its policy on the device: moe_cache_decode then applies the
+ * policy to the router's picks in a one-thread kernel and copies the misses with a
+ * kernel that reads the host tier through its device mapping, all in stream order on
+ * `stream`, so a decode row never waits for the host and can be captured in a graph.
+ * The policy is the one above, with a request counter per layer (the order it gives
+ * within a layer is the same).
+ *   device_state  device memory of moe_cache_device_state_bytes(...) bytes (256-byte
+ *                 aligned), owned by the caller; it holds the frequencies, the slots'
+ *                 experts and last uses, the counters and the last request's misses
+ *   host_pool     pinned host memory that is mapped on the device (hipHostMalloc,
+ *                 torch pin_memory); MOE_ERR_INVALID_ARG if it is not
+ * Creation initialises the state and the slot tables on `stream` and waits for it.
+ * moe_cache_decode ignores copy_stream and pass_tables on such a cache;
+ * moe_cache_acquire and moe_cache_lookup return MOE_ERR_INVALID_ARG (the policy is not
+ * on the host); moe_cache_stats synchronises the device and reads the counters. Decode
+ * rows of one cache must be enqueued on one stream (the requests are applied in stream
+ * order). moe_cache_device_state_bytes returns 0 for invalid sizes.
+ */
+uint64_t moe_cache_device_state_bytes(int32_t n_layers, int32_t n_experts, int32_t slots);
+moe_status moe_cache_create_device(int32_t n_layers, int32_t n_experts, int32_t slots, uint64_t blob_stride,
+                                   const uint8_t* host_pool, uint8_t* device_slots, uint32_t* slot_tables,
+                                   void* device_state, uint64_t state_bytes, void* stream,
+                                   moe_expert_cache** cache);
+
 /* The slot of each expert idx_host[0..n) of `layer` as the cache stands (-1: not
  * resident), without counting a request or changing anything; host-side only. A
  * following moe_cache_acquire naming these experts keeps every resident one in its

@@ -22,6 +22,8 @@ __all__ = [
     "moe_status_string",
     "moe_check_device_error",
     "moe_cache_create", "moe_cache_acquire", "moe_cache_stats", "moe_cache_destroy",
+    "moe_cache_create_device", "moe_cache_device_state_bytes", "moe_cache_lookup", "moe_cache_decode",
+    "moe_shared_expert_decode", "moe_combine_decode",
     "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED_SHAPE", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
     "MOE_ERR_DEVICE_CHECK", "MOE_F32", "MOE_BF16", "MOE_DEVERR_BAD_SLOT",
 ]
@@ -107,6 +109,8 @@ def lib() -> C.CDLL:
             "moe_status_string": (C.c_char_p, [st]),
             "moe_check_device_error": (st, [_P, C.POINTER(C.c_uint32)]),
             "moe_cache_create": (st, [i32, i32, i32, u64, _P, _P, _P, C.POINTER(_P)]),
+            "moe_cache_device_state_bytes": (u64, [i32, i32, i32]),
+            "moe_cache_create_device": (st, [i32, i32, i32, u64, _P, _P, _P, _P, u64, _P, C.POINTER(_P)]),
             "moe_cache_acquire": (st, [_P, i32, _P, i32, _P, _P, _P]),
             "moe_cache_lookup": (st, [_P, i32, _P, i32, _P]),
             "moe_cache_decode": (st, [_P, i32, S, _P, _P, _P, st, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P,
@@ -321,6 +325,22 @@ def moe_cache_create(n_layers: int, n_experts: int, slots: int, blob_stride: int
     hp = None if host_pool is None else host_pool.data_ptr()
     _check(lib().moe_cache_create(n_layers, n_experts, slots, blob_stride, hp, _dptr(device_slots),
                                   _dptr(slot_tables), C.byref(h)), "moe_cache_create")
+    return h.value
+
+
+def moe_cache_device_state_bytes(n_layers: int, n_experts: int, slots: int) -> int:
+    return int(lib().moe_cache_device_state_bytes(n_layers, n_experts, slots))
+
+
+def moe_cache_create_device(n_layers: int, n_experts: int, slots: int, blob_stride: int, host_pool, device_slots,
+                            slot_tables, device_state, stream=None) -> int:
+    """The cache with its policy on the device (see moe.h). host_pool: a pinned host torch
+    uint8 tensor; device_slots, slot_tables, device_state: GPU tensors."""
+    h = C.c_void_p()
+    _check(lib().moe_cache_create_device(n_layers, n_experts, slots, blob_stride, host_pool.data_ptr(),
+                                         _dptr(device_slots), _dptr(slot_tables), _dptr(device_state),
+                                         device_state.numel() * device_state.element_size(), _stream(stream),
+                                         C.byref(h)), "moe_cache_create_device")
     return h.value
 
 

@@ -24,6 +24,7 @@
 #include <new>
 #include <vector>
 
+#include "cache_device.h"
 #include "moe.h"
 
 struct moe_expert_cache {
@@ -33,6 +34,11 @@ struct moe_expert_cache {
   uint8_t* dev_slots = nullptr;        // [L][S] blobs, device memory
   uint32_t* dev_tables = nullptr;      // [L][E] device slot tables
   bool host_only = false;              // no device side: the policy alone (for tests)
+  // the policy on the device instead (moe_cache_create_device): its state, and the
+  // device address of the host tier the fills read
+  bool device_policy = false;
+  qmoe::CacheDevState dstate{};
+  const uint8_t* host_pool_dev = nullptr;
   std::vector<uint32_t> freq;          // [L][E] requests so far
   std::vector<int32_t> slot_of;        // [L][E] slot or -1
   std::vector<int32_t> expert_in;      // [L][S] expert or -1
@@ -127,7 +133,8 @@ moe_status moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t slots, 
 
 moe_status moe_cache_acquire(moe_expert_cache* c, int32_t layer, const int32_t* idx_host, int32_t n,
                              int32_t* slot_host, int32_t* n_misses, void* stream) {
-  if (!c || !idx_host || layer < 0 || layer >= c->L || n < 1 || n > c->S) return MOE_ERR_INVALID_ARG;
+  if (!c || c->device_policy || !idx_host || layer < 0 || layer >= c->L || n < 1 || n > c->S)
+    return MOE_ERR_INVALID_ARG;
   for (int32_t i = 0; i < n; ++i)
     if (idx_host[i] < 0 || idx_host[i] >= c->E) return MOE_ERR_INVALID_ARG;
   const size_t le = (size_t)layer * c->E, ls = (size_t)layer * c->S;
@@ -212,7 +219,7 @@ moe_status moe_cache_decode(moe_expert_cache* c, int32_t layer, const moe_shape*
   if (shape->n_experts != c->E || shape->top_k > c->S || shape->top_k > 16 || shape->top_k < 1)
     return MOE_ERR_INVALID_ARG;
   if (c->stride < moe_expert_blob_bytes(shape)) return MOE_ERR_INVALID_ARG;
-  if (copy_stream && !pass_tables) return MOE_ERR_INVALID_ARG;
+  if (copy_stream && !pass_tables && !c->device_policy) return MOE_ERR_INVALID_ARG;
   const int32_t E = c->E, S = c->S, k = shape->top_k;
   hipStream_t st = (hipStream_t)stream, cst = (hipStream_t)copy_stream;
   // the layer as the kernels see it: its slots as the pool, its slot table
@@ -221,6 +228,16 @@ moe_status moe_cache_decode(moe_expert_cache* c, int32_t layer, const moe_shape*
   moe_status r = moe_router_topk(shape, &view, x, x_dtype, 1, logit_offset, topk_idx, topk_w, nullptr, ws, ws_bytes,
                                  stream);
   if (r != MOE_OK) return r;
+  if (c->device_policy) {
+    // the policy and the copies on the device, in stream order: nothing comes back to the host
+    if (!qmoe::launch_cache_plan(c->dstate, layer, topk_idx, k, st) ||
+        !qmoe::launch_cache_fill(c->dstate, layer, c->host_pool_dev, c->dev_slots, k, st))
+      return MOE_ERR_HIP;
+    if ((r = moe_expert_ffn_decode(shape, &view, x, x_dtype, topk_idx, expert_out, ws, ws_bytes, stream)) != MOE_OK)
+      return r;
+    return moe_combine(shape, &view, x, x_dtype, 1, expert_out, nullptr, topk_w, y, residual_bf16, ws, ws_bytes,
+                       stream);
+  }
   // the host needs the picks
   if (hipMemcpyAsync(c->pick_stage, topk_idx, k * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
@@ -275,7 +292,7 @@ moe_status moe_cache_decode(moe_expert_cache* c, int32_t layer, const moe_shape*
 
 moe_status moe_cache_lookup(const moe_expert_cache* c, int32_t layer, const int32_t* idx_host, int32_t n,
                             int32_t* slot_host) {
-  if (!c || !idx_host || !slot_host || layer < 0 || layer >= c->L || n < 0) return MOE_ERR_INVALID_ARG;
+  if (!c || c->device_policy || !idx_host || !slot_host || layer < 0 || layer >= c->L || n < 0) return MOE_ERR_INVALID_ARG;
   for (int32_t i = 0; i < n; ++i)
     if (idx_host[i] < 0 || idx_host[i] >= c->E) return MOE_ERR_INVALID_ARG;
   const int32_t* slot_of = c->slot_of.data() + (size_t)layer * c->E;
@@ -285,15 +302,67 @@ moe_status moe_cache_lookup(const moe_expert_cache* c, int32_t layer, const int3
 
 moe_status moe_cache_stats(const moe_expert_cache* c, uint64_t* hits, uint64_t* misses, uint64_t* bytes_copied) {
   if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->device_policy) {
+    uint64_t v[3];
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(v, c->dstate.stats, sizeof v, hipMemcpyDeviceToHost) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (hits) *hits = v[0];
+    if (misses) *misses = v[1];
+    if (bytes_copied) *bytes_copied = v[2];
+    return MOE_OK;
+  }
   if (hits) *hits = c->hits;
   if (misses) *misses = c->misses;
   if (bytes_copied) *bytes_copied = c->bytes;
   return MOE_OK;
 }
 
+uint64_t moe_cache_device_state_bytes(int32_t n_layers, int32_t n_experts, int32_t slots) {
+  if (n_layers < 1 || n_experts < 1 || n_experts > 256 || slots < 1 || slots > n_experts) return 0;
+  return qmoe::cache_dev_state_bytes(n_layers, n_experts, slots);
+}
+
+moe_status moe_cache_create_device(int32_t n_layers, int32_t n_experts, int32_t slots, uint64_t blob_stride,
+                                   const uint8_t* host_pool, uint8_t* device_slots, uint32_t* slot_tables,
+                                   void* device_state, uint64_t state_bytes, void* stream, moe_expert_cache** cache) {
+  if (!cache) return MOE_ERR_INVALID_ARG;
+  *cache = nullptr;
+  if (n_layers < 1 || n_experts < 1 || n_experts > 256 || slots < 1 || slots > n_experts) return MOE_ERR_INVALID_ARG;
+  if (!device_slots || !slot_tables || !host_pool || !device_state || blob_stride == 0 || blob_stride % 256 ||
+      ((uintptr_t)device_state & 255u) || ((uintptr_t)slot_tables & 3u))
+    return MOE_ERR_INVALID_ARG;
+  if (state_bytes < qmoe::cache_dev_state_bytes(n_layers, n_experts, slots)) return MOE_ERR_WORKSPACE;
+  // the fills read the host tier from the device: it must be mapped
+  void* dev_view = nullptr;
+  if (hipHostGetDevicePointer(&dev_view, const_cast<uint8_t*>(host_pool), 0) != hipSuccess || !dev_view) {
+    (void)hipGetLastError();
+    return MOE_ERR_INVALID_ARG;
+  }
+  moe_expert_cache* c = new (std::nothrow) moe_expert_cache;
+  if (!c) return MOE_ERR_INVALID_ARG;
+  c->L = n_layers;
+  c->E = n_experts;
+  c->S = slots;
+  c->stride = blob_stride;
+  c->host_pool = host_pool;
+  c->host_pool_dev = static_cast<const uint8_t*>(dev_view);
+  c->dev_slots = device_slots;
+  c->dev_tables = slot_tables;
+  c->device_policy = true;
+  c->dstate = qmoe::cache_dev_state(device_state, slot_tables, n_layers, n_experts, slots, blob_stride);
+  hipStream_t st = (hipStream_t)stream;
+  if (!qmoe::launch_cache_init(c->dstate, st) || hipStreamSynchronize(st) != hipSuccess) {
+    release(c);
+    return MOE_ERR_HIP;
+  }
+  *cache = c;
+  return MOE_OK;
+}
+
 moe_status moe_cache_destroy(moe_expert_cache* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
-  if (!c->host_only)
+  if (!c->host_only && !c->device_policy)
     for (int32_t l = 0; l < c->L; ++l)
       if (c->staged_live[l] && hipEventSynchronize(c->staged[l]) != hipSuccess) {
         release(c);

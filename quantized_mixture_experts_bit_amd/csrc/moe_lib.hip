@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "cache_device.h"
 #include "common.h"
 #include "decode_fused.h"
 #include "decode_kernels.h"
@@ -17,6 +18,237 @@
 #include "router_kernels.h"
 
 using namespace qmoe;
+
+// ------------------------------------------------------------------ expert cache, device policy
+
+namespace qmoe {
+
+namespace {
+inline size_t cache_align(size_t v) { return (v + 255) & ~(size_t)255; }
+}  // namespace
+
+uint64_t cache_dev_state_bytes(int L, int E, int S) {
+  size_t o = 0;
+  o = cache_align(o + sizeof(uint32_t) * (size_t)L * E);          // freq
+  o = cache_align(o + sizeof(int32_t) * (size_t)L * S);           // expert_in
+  o = cache_align(o + sizeof(uint64_t) * (size_t)L * S);          // last_use
+  o = cache_align(o + sizeof(uint64_t) * (size_t)L);              // clock
+  o = cache_align(o + sizeof(uint32_t) * (1 + 2 * kCacheMaxPicks));  // miss list
+  o = cache_align(o + sizeof(uint64_t) * 3);                      // stats
+  return o;
+}
+
+CacheDevState cache_dev_state(void* base, uint32_t* tables, int L, int E, int S, uint64_t stride) {
+  CacheDevState st;
+  uint8_t* b = static_cast<uint8_t*>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = b + o;
+    o = cache_align(o + bytes);
+    return p;
+  };
+  st.tables = tables;
+  st.freq = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)L * E));
+  st.expert_in = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)L * S));
+  st.last_use = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)L * S));
+  st.clock = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)L));
+  st.miss = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (1 + 2 * kCacheMaxPicks)));
+  st.stats = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 3));
+  st.L = L;
+  st.E = E;
+  st.S = S;
+  st.stride = stride;
+  return st;
+}
+
+__global__ __launch_bounds__(256) void k_cache_init(CacheDevState st) {
+  const size_t LE = (size_t)st.L * st.E, LS = (size_t)st.L * st.S;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < LE + LS; i += (size_t)gridDim.x * 256) {
+    if (i < LE) {
+      st.tables[i] = (uint32_t)st.S;
+      st.freq[i] = 0u;
+    } else {
+      st.expert_in[i - LE] = -1;
+      st.last_use[i - LE] = 0u;
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int l = threadIdx.x; l < st.L; l += 256) st.clock[l] = 0u;
+    if (threadIdx.x < 1 + 2 * kCacheMaxPicks) st.miss[threadIdx.x] = 0u;
+    if (threadIdx.x < 3) st.stats[threadIdx.x] = 0u;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t w = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), o, 64) << 32) |
+                       (uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
+    v = min(v, w);
+  }
+  return v;
+}
+
+// The policy for one request, in request order (the host policy's rule). The layer's
+// state is staged in LDS by the whole workgroup; one wave applies the requests, each
+// lane holding slots lane, lane + 64, ... for the searches (the lowest never-used slot;
+// else the smallest (frequency, last use, id) among the slots whose expert the request
+// does not name, as three wave minima); lane 0 makes the updates; then the state goes
+// back. E, S <= 256.
+__global__ __launch_bounds__(256) void k_cache_plan(CacheDevState st, int layer, const int32_t* __restrict__ picks,
+                                                    int n) {
+  __shared__ uint32_t tab[256], fq[256];
+  __shared__ int32_t ein[256];
+  __shared__ uint64_t lu[256];
+  __shared__ int32_t req[kCacheMaxPicks];
+  const int E = st.E, S = st.S, t = threadIdx.x;
+  uint32_t* table = st.tables + (size_t)layer * E;
+  uint32_t* freq = st.freq + (size_t)layer * E;
+  int32_t* expert_in = st.expert_in + (size_t)layer * S;
+  uint64_t* last_use = st.last_use + (size_t)layer * S;
+  for (int i = t; i < E; i += 256) {
+    tab[i] = table[i];
+    fq[i] = freq[i];
+  }
+  for (int i = t; i < S; i += 256) {
+    ein[i] = expert_in[i];
+    lu[i] = last_use[i];
+  }
+  if (t < n) req[t] = picks[t];
+  __syncthreads();
+  if (t < 64) {
+    const int lane = t;
+    const uint64_t now = st.clock[layer] + 1;
+    uint32_t named[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int rq[kCacheMaxPicks];
+    int m = 0;
+    for (int i = 0; i < n; ++i) {
+      const int e = req[i];
+      if (e < 0 || e >= E) {  // not from the router; nothing to make resident for it
+        if (lane == 0) flag_device_error(2u);
+        continue;
+      }
+      rq[m++] = e;
+      if (!((named[e >> 5] >> (e & 31)) & 1u) && lane == 0) fq[e] += 1u;
+      named[e >> 5] |= 1u << (e & 31);
+    }
+    uint32_t misses = 0, hits = 0;
+    for (int i = 0; i < m; ++i) {
+      const int e = rq[i];
+      int s = (int)tab[e];
+      if (s < S) {
+        ++hits;
+      } else {
+        uint32_t free_j = 0xffffffffu;
+        for (int j = lane; j < S; j += 64)
+          if (ein[j] < 0) free_j = min(free_j, (uint32_t)j);
+        free_j = wave_min_u32(free_j);
+        if (free_j != 0xffffffffu) {
+          s = (int)free_j;
+        } else {
+          // every slot is in use: the victim among the experts the request does not name
+          uint32_t f = 0xffffffffu;
+          for (int j = lane; j < S; j += 64) {
+            const int v = ein[j];
+            if (!((named[v >> 5] >> (v & 31)) & 1u)) f = min(f, fq[v]);
+          }
+          f = wave_min_u32(f);
+          uint64_t u = ~0ull;
+          for (int j = lane; j < S; j += 64) {
+            const int v = ein[j];
+            if (!((named[v >> 5] >> (v & 31)) & 1u) && fq[v] == f) u = min(u, lu[j]);
+          }
+          u = wave_min_u64(u);
+          uint32_t id = 0xffffffffu;
+          for (int j = lane; j < S; j += 64) {
+            const int v = ein[j];
+            if (!((named[v >> 5] >> (v & 31)) & 1u) && fq[v] == f && lu[j] == u) id = min(id, (uint32_t)v);
+          }
+          id = wave_min_u32(id);
+          if (id == 0xffffffffu) {  // unreachable while n <= S (checked on the host)
+            if (lane == 0) flag_device_error(1u);
+            continue;
+          }
+          s = (int)tab[id];
+        }
+        if (lane == 0) {
+          if (ein[s] >= 0) tab[ein[s]] = (uint32_t)S;
+          ein[s] = e;
+          tab[e] = (uint32_t)s;
+          st.miss[1 + 2 * misses] = (uint32_t)e;
+          st.miss[2 + 2 * misses] = (uint32_t)s;
+        }
+        ++misses;
+      }
+      if (lane == 0) lu[s] = now;
+    }
+    if (lane == 0) {
+      st.clock[layer] = now;
+      st.miss[0] = misses;
+      st.stats[0] += hits;
+      st.stats[1] += misses;
+      st.stats[2] += (uint64_t)misses * st.stride;
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < E; i += 256) {
+    table[i] = tab[i];
+    freq[i] = fq[i];
+  }
+  for (int i = t; i < S; i += 256) {
+    expert_in[i] = ein[i];
+    last_use[i] = lu[i];
+  }
+}
+
+// Workgroup b copies part b % kCacheCopyBlocks of miss b / kCacheCopyBlocks (16-byte
+// words, four loads in flight per thread); workgroups past the plan's misses return.
+__global__ __launch_bounds__(256) void k_cache_fill(CacheDevState st, int layer, const uint8_t* host_pool_dev,
+                                                    uint8_t* dev_slots) {
+  const uint32_t i = blockIdx.x / kCacheCopyBlocks, part = blockIdx.x % kCacheCopyBlocks;
+  if (i >= st.miss[0]) return;
+  const uint32_t e = st.miss[1 + 2 * i], s = st.miss[2 + 2 * i];
+  const uint4* src = reinterpret_cast<const uint4*>(host_pool_dev + ((size_t)layer * st.E + e) * st.stride);
+  uint4* dst = reinterpret_cast<uint4*>(dev_slots + ((size_t)layer * st.S + s) * st.stride);
+  const uint64_t words = st.stride / 16, step = (uint64_t)kCacheCopyBlocks * 256;
+  uint64_t j = (uint64_t)part * 256 + threadIdx.x;
+  for (; j + 3 * step < words; j += 4 * step) {
+    const uint4 v0 = src[j], v1 = src[j + step], v2 = src[j + 2 * step], v3 = src[j + 3 * step];
+    dst[j] = v0;
+    dst[j + step] = v1;
+    dst[j + 2 * step] = v2;
+    dst[j + 3 * step] = v3;
+  }
+  for (; j < words; j += step) dst[j] = src[j];
+}
+
+bool launch_cache_init(const CacheDevState& st, hipStream_t stream) {
+  const size_t n = (size_t)st.L * st.E + (size_t)st.L * st.S;
+  const int grid = (int)std::min<size_t>(1024, std::max<size_t>(1, (n + 255) / 256));
+  k_cache_init<<<grid, 256, 0, stream>>>(st);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_cache_plan(const CacheDevState& st, int layer, const int32_t* picks, int n, hipStream_t stream) {
+  if (n < 1 || n > kCacheMaxPicks || n > st.S) return false;
+  if (st.E > 256 || st.S > 256) return false;
+  k_cache_plan<<<1, 256, 0, stream>>>(st, layer, picks, n);
+  return hipGetLastError() == hipSuccess;
+}
+
+bool launch_cache_fill(const CacheDevState& st, int layer, const uint8_t* host_pool_dev, uint8_t* dev_slots,
+                       int n_max, hipStream_t stream) {
+  if (n_max < 1 || n_max > kCacheMaxPicks || st.stride % 16) return false;
+  k_cache_fill<<<n_max * kCacheCopyBlocks, 256, 0, stream>>>(st, layer, host_pool_dev, dev_slots);
+  return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace qmoe
 
 // Decode workspace of moe_layer_decode_noalloc (see "static scratch" below).
 constexpr size_t kStaticScratchBytes = 4u << 20;

@@ -19,7 +19,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MOE_SLOT_SKIP, as_shape, moe_cache_acquire, moe_cache_create, moe_cache_decode, moe_cache_destroy,
+from . import (MOE_SLOT_SKIP, as_shape, moe_cache_acquire, moe_cache_create, moe_cache_create_device,
+               moe_cache_decode, moe_cache_destroy, moe_cache_device_state_bytes,
                moe_cache_stats, moe_combine, moe_expert_blob_bytes, moe_expert_ffn_prefill_chunk, moe_group_by_expert,
                moe_layer, moe_matrix4_bytes, moe_matrix8_bytes, moe_pack_matrix4, moe_pack_matrix8,
                moe_router_blob_bytes, moe_router_topk, moe_shared_blob_bytes)
@@ -195,15 +196,24 @@ class CachedLayer:
 
 class TieredStore:
     """Fast tier: `slots` HBM expert slots per layer in front of a HostExpertPool,
-    managed by the library's cache (moe_cache_*)."""
+    managed by the library's cache (moe_cache_*). device_policy=True keeps the
+    replacement policy on the device (moe_cache_create_device): decode rows then never
+    wait for the host (and can be graph-captured); the prefill passes need the host
+    policy."""
 
-    def __init__(self, host: HostExpertPool, slots: int, device="cuda"):
+    def __init__(self, host: HostExpertPool, slots: int, device="cuda", device_policy: bool = False):
         self.shape, self.host, self.slots, self.stride = host.shape, host, slots, host.stride
         E, L = host.shape.n_experts, host.n_layers
         dev = torch.device(device)
+        self.device_policy = device_policy
         self.dev_slots = torch.empty(L * slots * self.stride, dtype=torch.uint8, device=dev)
         self.tables = torch.empty(L * E, dtype=torch.int32, device=dev)
-        self.handle = moe_cache_create(L, E, slots, self.stride, host.buf, self.dev_slots, self.tables)
+        if device_policy:
+            self.state = torch.empty(moe_cache_device_state_bytes(L, E, slots), dtype=torch.uint8, device=dev)
+            self.handle = moe_cache_create_device(L, E, slots, self.stride, host.buf, self.dev_slots, self.tables,
+                                                  self.state)
+        else:
+            self.handle = moe_cache_create(L, E, slots, self.stride, host.buf, self.dev_slots, self.tables)
 
     def layer(self, l: int, router: torch.Tensor, shared: torch.Tensor) -> CachedLayer:
         return CachedLayer(self, l, router, shared)

@@ -151,3 +151,25 @@ def test_cache_decode_needs_a_device_cache():
         assert q.lib().moe_cache_decode(None, 0, C.byref(s), *args) == q.MOE_ERR_INVALID_ARG
     finally:
         q.moe_cache_destroy(h)
+
+
+def test_device_policy_sizes_and_arguments():
+    import ctypes as C
+    assert q.moe_cache_device_state_bytes(0, 128, 16) == 0
+    assert q.moe_cache_device_state_bytes(2, 300, 16) == 0
+    assert q.moe_cache_device_state_bytes(2, 128, 129) == 0
+    a = q.moe_cache_device_state_bytes(2, 128, 16)
+    b = q.moe_cache_device_state_bytes(4, 128, 16)
+    assert a > 2 * 128 * 4 + 2 * 16 * 12 and b > a and a % 256 == 0
+    lib, h = q.lib(), C.c_void_p()
+    # rejected before any HIP call: sizes, missing or misaligned buffers, too small a state
+    assert lib.moe_cache_create_device(0, 128, 16, 3346432, 0x1000, 0x2000, 0x3000, 0x4000, a, None,
+                                       C.byref(h)) == q.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_create_device(2, 128, 16, 3346432, None, 0x2000, 0x3000, 0x4000, a, None,
+                                       C.byref(h)) == q.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_create_device(2, 128, 16, 3346432, 0x1000, 0x2000, 0x3000, 0x4010, a, None,
+                                       C.byref(h)) == q.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_create_device(2, 128, 16, 3346430, 0x1000, 0x2000, 0x3000, 0x4000, a, None,
+                                       C.byref(h)) == q.MOE_ERR_INVALID_ARG
+    assert lib.moe_cache_create_device(2, 128, 16, 3346432, 0x1000, 0x2000, 0x3000, 0x4000, a - 256, None,
+                                       C.byref(h)) == q.MOE_ERR_WORKSPACE

@@ -207,3 +207,105 @@ def test_decode_experts_skip_entries():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), full.view(torch.int32))
     assert q.moe_check_device_error() == 0
+
+
+def _device_policy_setup(shape, n_layers, slots):
+    layers = [synth.make_layer(shape, seed=5, layer=l) for l in range(n_layers)]
+    resident = upload_layers(shape, layers, device())
+    host = HostExpertPool(shape, n_layers)
+    for l, L in enumerate(layers):
+        host.load_layer(l, L)
+    return layers, resident, host
+
+
+@pytest.mark.parametrize("zipf", [False, True], ids=["uniform", "zipf"])
+def test_device_policy_decode_matches_resident_and_host_policy(zipf):
+    """The cache with its policy on the device: the same bits as the resident pool, and
+    after every request the same residency as the host policy given the same picks."""
+    shape, n_layers, slots, tokens = synth.GEMMA4, 2, 12, 10
+    k, E = shape.top_k, shape.n_experts
+    layers, resident, host = _device_policy_setup(shape, n_layers, slots)
+    store = TieredStore(host, slots, device(), device_policy=True)
+    policy = q.moe_cache_create(n_layers, E, slots)  # the host policy alone, as the model
+    try:
+        cached = [store.layer(l, resident[l].router, resident[l].shared) for l in range(n_layers)]
+        offs = [torch.from_numpy(synth.make_zipf_offset(shape, seed=0, layer=l)).to(device()) if zipf else None
+                for l in range(n_layers)]
+        ws = workspace(shape, 1)
+        olayers = [O.OracleLayer(L) for L in layers]
+        total_miss = 0
+        for t in range(tokens):
+            for l in range(n_layers):
+                x_np = synth.make_x(shape, 1, seed=300 + t, stream=l, dtype="bf16")
+                x = to_dev_x(x_np)
+                i0, e0, y0, _ = decode_split(shape, resident[l].c, x, offs[l], ws)
+                i1, e1, y1, miss = decode_split(shape, None, x, offs[l], ws, cached[l])
+                np.testing.assert_array_equal(i1, i0)
+                assert np.array_equal(e1.view(np.uint32), e0.view(np.uint32)), (t, l)
+                assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32)), (t, l)
+                total_miss += miss
+                want_miss = q.moe_cache_acquire(policy, l, i1.astype(np.int32))
+                assert miss == want_miss, (t, l)
+                table = store.tables.view(n_layers, E)[l].cpu().numpy()
+                want = q.moe_cache_lookup(policy, l, np.arange(E, dtype=np.int32))
+                np.testing.assert_array_equal(np.where(table < slots, table, -1), want)
+                if t % 3 == 0:
+                    off_np = None if offs[l] is None else offs[l].cpu().numpy()
+                    ref = O.moe_rows(olayers[l], x_np, offset=off_np)
+                    if check_topk(i1[None], ref, k)[0]:
+                        ref = O.moe_rows(olayers[l], x_np, offset=off_np, idx=i1[None])
+                    assert rel_err(y1, ref["y"][0]) <= REL_TOL, (t, l)
+        assert q.moe_check_device_error() == 0
+        hits, misses, nbytes = store.stats()
+        assert hits + misses == tokens * n_layers * k and misses == total_miss
+        assert nbytes == misses * store.stride and misses > n_layers * slots  # evictions happened
+    finally:
+        store.close()
+        q.moe_cache_destroy(policy)
+
+
+def test_device_policy_decode_graph_replays():
+    """A token through two cached layers captured once and replayed token after token
+    (x rewritten before each replay) gives the bits of the same calls run eagerly on a
+    second cache with the same history."""
+    shape, n_layers, slots, tokens = synth.GEMMA4, 2, 12, 6
+    k, d = shape.top_k, shape.d_model
+    layers, resident, host = _device_policy_setup(shape, n_layers, slots)
+    stores = [TieredStore(host, slots, device(), device_policy=True) for _ in range(2)]
+    try:
+        cl = [[s.layer(l, resident[l].router, resident[l].shared) for l in range(n_layers)] for s in stores]
+        ws = [workspace(shape, 1) for _ in range(2)]
+        bufs = [dict(x=torch.empty(1, d, dtype=torch.bfloat16, device=device()), idx=empty_i32(n_layers, k),
+                     w=empty_f32(n_layers, k), eo=empty_f32(k, d), y=empty_f32(n_layers, d)) for _ in range(2)]
+
+        def token(i):
+            b = bufs[i]
+            for l in range(n_layers):
+                cl[i][l].decode(b["x"], None, b["idx"][l], b["w"][l], b["eo"], b["y"][l], b["x"], ws[i])
+
+        xs = [to_dev_x(synth.make_x(shape, 1, seed=900 + t, dtype="bf16")) for t in range(tokens + 1)]
+        # store 1: one eager token (the code objects load), then captured
+        bufs[1]["x"].copy_(xs[0])
+        token(1)
+        bufs[0]["x"].copy_(xs[0])
+        token(0)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            token(1)  # the capture itself runs nothing
+        for t in range(1, tokens + 1):
+            bufs[0]["x"].copy_(xs[t])
+            token(0)
+            bufs[1]["x"].copy_(xs[t])
+            g.replay()
+            torch.cuda.synchronize()
+            for n in ("idx", "w", "y", "x"):
+                a, b = bufs[0][n], bufs[1][n]
+                assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                                   b.view(torch.int16) if b.dtype == torch.bfloat16 else b), (t, n)
+        assert q.moe_check_device_error() == 0
+        assert stores[0].stats() == stores[1].stats()
+    finally:
+        for s in stores:
+            s.close()
