@@ -314,7 +314,7 @@ moe_status moe_stack_decode(const moe_shape* shape, const moe_layer* layers, int
 /*
  * moe_layer_decode for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
- * workspace: its scratch is a static device array of the library (4 MiB per GPU the
+ * workspace: its scratch is a static device array of the library (5 MiB per GPU the
  * library runs on, held until the process ends), found once per device with
  * hipGetSymbolAddress. It calls no hipMalloc, hipFree or allocating routine. Same
  * arguments and results as moe_layer_decode without ws/ws_bytes; the caller still

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ topk
 // per thread; the row's positions and weights are uniform, and every routed output of
 // the thread is loaded before the first one is added (top_k <= kMaxTopK).
 constexpr int kMaxTopK = 16;
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ shared_out,
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ shared_out, int shared_parts,
                                                  const float* __restrict__ expert_out,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ topk_w, int rows, int d, int top_k,
@@ -172,7 +172,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ share
       e[k] = *reinterpret_cast<const float4*>(expert_out + (size_t)max(pos[k], 0) * d + n);
     }
   }
+  // the shared expert: its K parts (shared_out + p * rows * d) added in order
   float4 v = *reinterpret_cast<const float4*>(shared_out + (size_t)r * d + n);
+  for (int p = 1; p < shared_parts; ++p) {
+    const float4 u = *reinterpret_cast<const float4*>(shared_out + ((size_t)p * rows + r) * d + n);
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     if (k < top_k && pos[k] >= 0) {

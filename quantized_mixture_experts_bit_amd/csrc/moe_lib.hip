@@ -251,7 +251,7 @@ bool launch_cache_fill(const CacheDevState& st, int layer, const uint8_t* host_p
 }  // namespace qmoe
 
 // Decode workspace of moe_layer_decode_noalloc (see "static scratch" below).
-constexpr size_t kStaticScratchBytes = 4u << 20;
+constexpr size_t kStaticScratchBytes = 5u << 20;
 static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
@@ -336,7 +336,7 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.shared_part = take(sizeof(float) * (size_t)dc.Ps * d);
   w.pf_H = take(sizeof(float) * R * k * s->d_ff);
   w.pf_Hs = take(sizeof(float) * R * s->d_ff_shared);
-  w.pf_shared_out = take(sizeof(float) * R * d);
+  w.pf_shared_out = take(sizeof(float) * kSharedDownParts * R * d);
   w.pf_hmaxp = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
   w.pf_Hh = take(sizeof(uint16_t) * R * ((size_t)k * s->d_ff + s->d_ff_shared));
   w.pf_hsc = take(sizeof(float) * R * (k + 1));
@@ -858,7 +858,7 @@ moe_status moe_combine(const moe_shape* s, const moe_layer* L, const void* x, mo
     launch_prefill(A, (const uint16_t*)x, false, true, true, hs);
   else
     launch_prefill(A, (const float*)x, false, true, true, hs);
-  k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, topk_w, rows,
+  k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, kSharedDownParts, expert_out, inv_perm, topk_w, rows,
                                                                  s->d_model, s->top_k, y, residual);
   return launched();
 }
@@ -944,7 +944,7 @@ moe_status moe_layer_prefill(const moe_shape* s, const moe_layer* L, const void*
     launch_prefill(A, (const uint16_t*)x, true, true, false, hs);
   else
     launch_prefill(A, (const float*)x, true, true, false, hs);
-  k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, expert_out, inv_perm, w, rows,
+  k_combine<<<dim3(cdiv(s->d_model / 4, 256), rows), 256, 0, hs>>>(A.shared_out, kSharedDownParts, expert_out, inv_perm, w, rows,
                                                                  s->d_model, s->top_k, y, residual);
   return launched();
 }

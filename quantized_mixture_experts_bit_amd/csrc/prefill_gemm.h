@@ -36,6 +36,10 @@ namespace qmoe {
 
 constexpr int kLdsStride = 72;  // halfs per LDS row: 64 + 8 padding (144 B) against bank conflicts
 constexpr int kRing = 4;        // weight groups in flight per wavefront
+// The shared expert's down projection runs in this many K parts (d_ff_shared / 3 is the
+// routed experts' d_ff in the Gemma-like shape), each a work item of its own, so its
+// items are no longer than a routed expert's; the combine adds the parts in order.
+constexpr int kSharedDownParts = 3;
 constexpr int kXcds = 8;        // accelerator dies, each with its own L2
 constexpr int kMaxG = 96;       // groups of the reduction: d_model <= 6144
 
@@ -73,7 +77,7 @@ struct PrefillArgs {
   uint16_t* Hh;           // fp16 of h * hsc: routed [rows*top_k][f], then shared [rows][fs]
   float* hsc;             // power-of-two row scale of Hh: routed [rows*top_k], then shared [rows]
   float* expert_out;      // [rows*top_k][d]
-  float* shared_out;      // [rows][d]
+  float* shared_out;      // [kSharedDownParts][rows][d]: the shared expert's down in K parts
 };
 
 // 64-row tile -> (expert, first sorted position, row count); expert -1 = shared
@@ -587,13 +591,17 @@ struct DownSmem {
 // one staged H tile feeds twice the columns. With an odd number of blocks the last
 // item's second block repeats its first and is not stored.
 constexpr int kDownBlocks = 2;
-__device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, int np, bool shared, DownSmem& S) {
+__device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, int np, bool shared, int part,
+                                          DownSmem& S) {
   constexpr int RA = 4;
   auto& Hl = S.Hl;
   auto& rowinv = S.rowinv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int F = T.F, G = F / kGroup;
+  // K groups [gb, ge) of this item: all of a routed expert's, part `part` of the shared expert's
+  const int gp = (G + kSharedDownParts - 1) / kSharedDownParts;
+  const int gb = shared ? min(G, part * gp) : 0, ge = shared ? min(G, gb + gp) : G;
   const int nmb = (T.mrows + 15) >> 4;
   const int P = A.rows * A.top_k;
   const uint16_t* Hh = shared ? A.Hh + (size_t)P * A.f : A.Hh;
@@ -644,16 +652,23 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     v = dpp_add<0x4E, 0xf>(v);
     if (hq == 0) S.agL[buf][hr] = v;
   };
+  float* out = shared ? A.shared_out + (size_t)part * A.rows * A.d : A.expert_out;
+  if (ge <= gb) {  // an empty part (d_ff_shared under kSharedDownParts groups): zeros
+    if (tid < 64)
+      for (int m = 0; m < kDownBlocks && kDownBlocks * np + m < nblk; ++m)
+        for (int r = 0; r < T.mrows; ++r) out[(size_t)(T.m0 + r) * A.d + nbm[m] * 64 + tid] = 0.0f;
+    return;
+  }
   // prologue: the loads in the order the steady state issues them (weights of group
   // j, then activations of group j + 1), so the wait counts agree on entry
-  aload(ic<0>{}, 0);
+  aload(ic<0>{}, gb);
   static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
-    B.load(jc, wres, min(j, G - 1));
-    if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(j + 1, G - 1));
+    B.load(jc, wres, min(gb + j, ge - 1));
+    if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(gb + j + 1, ge - 1));
     if constexpr (j + 1 == RA) {
       astore(ic<0>{}, 0);
-      aload(ic<0>{}, min(RA, G - 1));
+      aload(ic<0>{}, min(gb + RA, ge - 1));
     }
   });
   __syncthreads();
@@ -678,7 +693,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
       s[m] = bf16_lo(B.sb[j][m]);
       bp[m] = bf16_hi(B.sb[j][m]);
     }
-    B.load(jc, wres, min(g + kRing, G - 1));
+    B.load(jc, wres, min(g + kRing, ge - 1));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if (mb < nmb) {
@@ -695,20 +710,19 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
       }
     }
     astore(ic<(j + 1) % RA>{}, buf ^ 1);
-    aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, G - 1));
+    aload(ic<(j + 1) % RA>{}, min(g + 1 + RA, ge - 1));
     __syncthreads();
   };
-  int g0 = 0;
-  for (; g0 + kRing <= G; g0 += kRing) {
+  int g0 = gb;
+  for (; g0 + kRing <= ge; g0 += kRing) {
     step(ic<0>{}, g0);
     step(ic<1>{}, g0 + 1);
     step(ic<2>{}, g0 + 2);
     step(ic<3>{}, g0 + 3);
   }
-  if (g0 < G) step(ic<0>{}, g0);
-  if (g0 + 1 < G) step(ic<1>{}, g0 + 1);
-  if (g0 + 2 < G) step(ic<2>{}, g0 + 2);
-  float* out = shared ? A.shared_out : A.expert_out;
+  if (g0 < ge) step(ic<0>{}, g0);
+  if (g0 + 1 < ge) step(ic<1>{}, g0 + 1);
+  if (g0 + 2 < ge) step(ic<2>{}, g0 + 2);
 #pragma unroll
   for (int m = 0; m < kDownBlocks; ++m) {
     if (kDownBlocks * np + m >= nblk) break;  // the repeated last block
@@ -729,21 +743,24 @@ __global__ __launch_bounds__(256, 2) void k_prefill_down(PrefillArgs A) {
   TileMap M;
   const int nrt = A.routed_mtiles > 0 ? tile_map_init(A, M) : 0;
   const int nc = (A.d / 64 + kDownBlocks - 1) / kDownBlocks;
-  const int ns = xcd_blocks(A.shared_mtiles, nc);
+  // the shared expert's items: (row tile, K part) pairs x column blocks
+  const int nsp = A.shared_mtiles * kSharedDownParts;
+  const int ns = xcd_blocks(nsp, nc);
   const int n = ns + xcd_blocks(nrt, nc);
   for (int item = blockIdx.x; item < n; item += gridDim.x) {
     const bool shared = item < ns;
-    int mt, nb;
+    int mt, nb, part = 0;
     MTile T;
     if (shared) {
-      xcd_item(item, A.shared_mtiles, nc, mt, nb);
-      if (mt >= A.shared_mtiles) continue;
-      shared_tile(A, mt, T);
+      xcd_item(item, nsp, nc, mt, nb);
+      if (mt >= nsp) continue;
+      part = mt % kSharedDownParts;
+      shared_tile(A, mt / kSharedDownParts, T);
     } else {
       xcd_item(item - ns, nrt, nc, mt, nb);
       if (mt >= nrt || !tile_at(A, M, mt, T)) continue;
     }
-    down_tile(A, T, nb, shared, S);
+    down_tile(A, T, nb, shared, part, S);
     __syncthreads();  // the next item reuses the LDS
   }
 }
