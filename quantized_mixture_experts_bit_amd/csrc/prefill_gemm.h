@@ -209,28 +209,41 @@ __device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Weight fragments of NM matrices in a ring of kRing groups: for wave row `row`
-// (0..63 within the 64-row block), the two code words of k-halves 0 and 1 and the
-// (scale, bias) pair, from tile g of the column block whose tiles start at the base
-// of wres[m]. The lane offsets are fixed; the group enters as a scalar offset.
-template <int NM>
+// Weight fragments of two 64-row blocks (gate and up of one column block, or two output
+// blocks of the down projection) in a ring of kRing groups, for wave row `row` (0..63
+// within a block). The matrix cores want, in lane 16c + n, code word c of row n's 16-byte
+// segment of each (block, k-half). Those words sit 16 bytes apart, so fetching them
+// directly takes four 4-byte loads whose 16-lane quarters each touch 256 bytes. Instead
+// every lane fetches one whole 16-byte segment: lanes 16q + n take k-half q & 1 of block
+// q >> 1 (16 lanes cover 256 contiguous bytes), and a 4 x 4 transpose across the four
+// 16-lane rows (two permlane32 and two permlane16 swaps) gives each lane its words. The
+// (scale, bias) words are loaded per lane as before. One buffer resource spans both
+// blocks, which start `mstride` bytes apart; the group enters as a scalar offset.
 struct BRing {
-  uint32_t cw[kRing][NM][2];
-  uint32_t sb[kRing][NM];
-  uint32_t vc, vs;  // lane offsets of the code word and of (s, b) within a tile
-  __device__ __forceinline__ void init(int row, int lane) {
-    vc = row * 16 + (lane >> 4) * 4;
-    vs = kTile4Codes + row * 4;
+  u32x4_t cw[kRing];  // as fetched; transposed when used
+  uint32_t sb[kRing][2];
+  uint32_t vc, vs[2];
+  __device__ __forceinline__ void init(int row, int lane, uint32_t mstride) {
+    vc = (uint32_t)(lane >> 5) * mstride + (uint32_t)((lane >> 4) & 1) * 1024u + (uint32_t)row * 16u;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) vs[m] = (uint32_t)m * mstride + kTile4Codes + (uint32_t)row * 4u;
   }
   template <int slot>
-  __device__ __forceinline__ void load(ic<slot>, const rsrc_t* wres, int g) {
+  __device__ __forceinline__ void load(ic<slot>, rsrc_t r, int g) {
+    const uint32_t so = (uint32_t)g * kTile4;
+    cw[slot] = bld16(r, vc, so);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const uint32_t so = (uint32_t)g * kTile4;
-      cw[slot][m][0] = bld4(wres[m], vc, so);
-      cw[slot][m][1] = bld4(wres[m], vc + 1024, so);
-      sb[slot][m] = bld4(wres[m], vs, so);
-    }
+    for (int m = 0; m < 2; ++m) sb[slot][m] = bld4(r, vs[m], so);
+  }
+  // the code words of a slot: element 2 m + h is k-half h of block m
+  template <int slot>
+  __device__ __forceinline__ u32x4_t codes(ic<slot>) const {
+    u32x4_t w = cw[slot];
+    const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);  // rows 2,3 of the first <-> rows 0,1 of the second
+    const auto b = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);  // rows 1,3 of the first <-> rows 0,2 of the second
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return u32x4_t{c[0], c[1], d[0], d[1]};
   }
 };
 
@@ -277,13 +290,10 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
 
   // weight rows of this wave: row 16*wave + lane%16 of the 64-row block fc of gate and up
   const int wrow = 16 * wave + (lane & 15);
-  rsrc_t wres[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    wres[m] = buf_rsrc(uniform_ptr(T.blob) + (uint64_t)m * m4_bytes(T.F, A.d) + (uint64_t)fc * G * kTile4,
-                       (uint32_t)G * kTile4);
-  BRing<2> B;
-  B.init(wrow, lane);
+  const uint32_t mstride = (uint32_t)m4_bytes(T.F, A.d);  // gate to up
+  const rsrc_t wres = buf_rsrc(uniform_ptr(T.blob) + (uint64_t)fc * G * kTile4, mstride + (uint32_t)G * kTile4);
+  BRing B;
+  B.init(wrow, lane, mstride);
 
   // activation staging: thread -> tile row tid/4, 16 values at column (tid%4)*16 of a group.
   // Rows past the tile's end repeat its first row: MFMA output rows depend on their
@@ -408,10 +418,11 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
         constexpr int j = j0 + p;
         bf16x8_t bfr[2][2];
         float s[2], bb[2];
+        const u32x4_t cw = B.codes(ic<j>{});
   #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          bfr[m][0] = codes_bf16(B.cw[j][m][0], nk);
-          bfr[m][1] = codes_bf16(B.cw[j][m][1], nk);
+          bfr[m][0] = codes_bf16(cw[2 * m], nk);
+          bfr[m][1] = codes_bf16(cw[2 * m + 1], nk);
           s[m] = bf16_lo(B.sb[j][m]);
           bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
         }
@@ -609,16 +620,15 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
 
   const int wrow = 16 * wave + (lane & 15);
   const int nblk = A.d / 64;
+  static_assert(kDownBlocks == 2, "the weight ring holds two blocks");
   int nbm[kDownBlocks];
-  rsrc_t wres[kDownBlocks];
 #pragma unroll
-  for (int m = 0; m < kDownBlocks; ++m) {
-    nbm[m] = min(kDownBlocks * np + m, nblk - 1);
-    wres[m] = buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nbm[m] * G * kTile4,
-                       (uint32_t)G * kTile4);
-  }
-  BRing<kDownBlocks> B;
-  B.init(wrow, lane);
+  for (int m = 0; m < kDownBlocks; ++m) nbm[m] = min(kDownBlocks * np + m, nblk - 1);
+  const uint32_t mstride = (uint32_t)(nbm[1] - nbm[0]) * G * kTile4;  // 0 for a repeated last block
+  const rsrc_t wres = buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nbm[0] * G * kTile4,
+                               mstride + (uint32_t)G * kTile4);
+  BRing B;
+  B.init(wrow, lane, mstride);
   if (tid < 64) rowinv[tid] = tid < T.mrows ? 1.0f / hsc[T.m0 + tid] : 1.0f;  // exact: powers of two
 
   // H staging: thread -> tile row tid/4, 16 halfs at column (tid%4)*16; rows past
@@ -686,10 +696,11 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     constexpr int buf = j & 1;
     f16x8_t b0[kDownBlocks], b1[kDownBlocks];
     float s[kDownBlocks], bp[kDownBlocks];
+    const u32x4_t cw = B.codes(jc);
 #pragma unroll
     for (int m = 0; m < kDownBlocks; ++m) {
-      b0[m] = codes_f16(B.cw[j][m][0], nk);
-      b1[m] = codes_f16(B.cw[j][m][1], nk);
+      b0[m] = codes_f16(cw[2 * m], nk);
+      b1[m] = codes_f16(cw[2 * m + 1], nk);
       s[m] = bf16_lo(B.sb[j][m]);
       bp[m] = bf16_hi(B.sb[j][m]);
     }
