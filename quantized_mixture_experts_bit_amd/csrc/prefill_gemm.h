@@ -46,6 +46,7 @@ constexpr int kMaxG = 96;       // groups of the reduction: d_model <= 6144
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // native 128-bit vector (HIP's uint4 is a struct: copies of it through register
 // arrays become private-memory copies that stay in scratch)
 
@@ -217,23 +218,29 @@ __device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
 // every lane fetches one whole 16-byte segment: lanes 16q + n take k-half q & 1 of block
 // q >> 1 (16 lanes cover 256 contiguous bytes), and a 4 x 4 transpose across the four
 // 16-lane rows (two permlane32 and two permlane16 swaps) gives each lane its words. The
-// (scale, bias) words are loaded per lane as before. One buffer resource spans both
-// blocks, which start `mstride` bytes apart; the group enters as a scalar offset.
+// (scale, bias) words take one load too: 16-lane row q fetches block q & 1's word of its
+// row, and one permlane16 swap of that register with itself puts block 0's word in every
+// row of one result and block 1's in every row of the other. One buffer resource spans
+// both blocks, which start `mstride` bytes apart; the group enters as a scalar offset.
 struct BRing {
   u32x4_t cw[kRing];  // as fetched; transposed when used
-  uint32_t sb[kRing][2];
-  uint32_t vc, vs[2];
+  uint32_t sb[kRing];
+  uint32_t vc, vs;
   __device__ __forceinline__ void init(int row, int lane, uint32_t mstride) {
     vc = (uint32_t)(lane >> 5) * mstride + (uint32_t)((lane >> 4) & 1) * 1024u + (uint32_t)row * 16u;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) vs[m] = (uint32_t)m * mstride + kTile4Codes + (uint32_t)row * 4u;
+    vs = (uint32_t)((lane >> 4) & 1) * mstride + kTile4Codes + (uint32_t)row * 4u;
   }
   template <int slot>
   __device__ __forceinline__ void load(ic<slot>, rsrc_t r, int g) {
     const uint32_t so = (uint32_t)g * kTile4;
     cw[slot] = bld16(r, vc, so);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) sb[slot][m] = bld4(r, vs[m], so);
+    sb[slot] = bld4(r, vs, so);
+  }
+  // the (scale, bias) words of a slot: element m is block m's
+  template <int slot>
+  __device__ __forceinline__ u32x2_t scales(ic<slot>) const {
+    const auto t = __builtin_amdgcn_permlane16_swap(sb[slot], sb[slot], false, false);
+    return u32x2_t{t[0], t[1]};
   }
   // the code words of a slot: element 2 m + h is k-half h of block m
   template <int slot>
@@ -419,12 +426,13 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
         bf16x8_t bfr[2][2];
         float s[2], bb[2];
         const u32x4_t cw = B.codes(ic<j>{});
+        const u32x2_t sbw = B.scales(ic<j>{});
   #pragma unroll
         for (int m = 0; m < 2; ++m) {
           bfr[m][0] = codes_bf16(cw[2 * m], nk);
           bfr[m][1] = codes_bf16(cw[2 * m + 1], nk);
-          s[m] = bf16_lo(B.sb[j][m]);
-          bb[m] = fmaf(-128.0f, s[m], bf16_hi(B.sb[j][m]));  // b - 128 s
+          s[m] = bf16_lo(sbw[m]);
+          bb[m] = fmaf(-128.0f, s[m], bf16_hi(sbw[m]));  // b - 128 s
         }
         B.load(ic<j>{}, wres, min(g + p + kRing, G - 1));
   #pragma unroll
@@ -697,12 +705,13 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     f16x8_t b0[kDownBlocks], b1[kDownBlocks];
     float s[kDownBlocks], bp[kDownBlocks];
     const u32x4_t cw = B.codes(jc);
+    const u32x2_t sbw = B.scales(jc);
 #pragma unroll
     for (int m = 0; m < kDownBlocks; ++m) {
       b0[m] = codes_f16(cw[2 * m], nk);
       b1[m] = codes_f16(cw[2 * m + 1], nk);
-      s[m] = bf16_lo(B.sb[j][m]);
-      bp[m] = bf16_hi(B.sb[j][m]);
+      s[m] = bf16_lo(sbw[m]);
+      bp[m] = bf16_hi(sbw[m]);
     }
     B.load(jc, wres, min(g + kRing, ge - 1));
 #pragma unroll
