@@ -390,7 +390,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
         if (g < G) {  // wave-uniform
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            if (g + c < G) S.xgL[(g + c) * 64 + r] = __uint_as_float(v[u][c]);
+            S.xgL[(g + c) * 64 + r] = g + c < G ? __uint_as_float(v[u][c]) : 0.0f;  // zeros up to a multiple of 4
         }
       }
     }
@@ -408,6 +408,23 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
       zero_acc(acc[mb][0]);
       zero_acc(acc[mb][1]);
     }
+    // The bias term sum_g (b_g - 128 s_g) X_g of four consecutive groups is one fp32
+    // 16x16x4 matrix product per row block and matrix: lane 16k + n collects column n's
+    // (b - 128 s) of the k-th group of the four in bsel (each group writes its own lane
+    // row), and the A operand is the group sums X of those groups from LDS (zero past G).
+    // Ring slot j holds group g0 + j with g0 a multiple of kRing, so j % 4 is the group's
+    // place among its four.
+    static_assert(kRing % 4 == 0, "a ring pass covers whole sets of four groups");
+    float bsel[2] = {0.0f, 0.0f};
+    auto bias4 = [&](int gq) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const float a4 = S.xgL[(gq + (lane >> 4)) * 64 + 16 * mb + (lane & 15)];
+  #pragma unroll
+        for (int m = 0; m < 2; ++m) acc[mb][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4, bsel[m], acc[mb][m], 0, 0, 0);
+      }
+      bsel[0] = bsel[1] = 0.0f;  // lanes of groups past G stay zero in a last partial set
+    };
 
     // One stage = SG K groups from LDS buffer (j0 / SG) & 1 and weight slots j0.. j0 + SG - 1:
     // per group the codes of its slot become MFMA operands and the slot is refilled with
@@ -433,6 +450,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
           bfr[m][1] = codes_bf16(cw[2 * m + 1], nk);
           s[m] = bf16_lo(sbw[m]);
           bb[m] = fmaf(-128.0f, s[m], bf16_hi(sbw[m]));  // b - 128 s
+          bsel[m] = (lane >> 4) == (j & 3) ? bb[m] : bsel[m];
         }
         B.load(ic<j>{}, wres, min(g + p + kRing, G - 1));
   #pragma unroll
@@ -440,8 +458,6 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
           const int ao = buf * kBuf + (16 * mb + (lane & 15)) * kStride + p * 64 + 8 * (lane >> 4);
           const bf16x8_t a0 = lds_frag<bf16x8_t>(&Xs[ao]);
           const bf16x8_t a1 = lds_frag<bf16x8_t>(&Xs[ao + 32]);
-          // group sums of rows 16 mb + 4 (lane / 16) + i, the rows of this lane's outputs
-          const f32x4_t ag = *reinterpret_cast<const f32x4_t*>(&S.xgL[(g + p) * 64 + 16 * mb + 4 * (lane >> 4)]);
           f32x4_t t[2];
   #pragma unroll
           for (int m = 0; m < 2; ++m) t[m] = mfma(a1, bfr[m][1], mfma(a0, bfr[m][0], f32x4_t{0.f, 0.f, 0.f, 0.f}));
@@ -454,8 +470,9 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
   #pragma unroll
           for (int m = 0; m < 2; ++m)
   #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[m][i], fmaf(bb[m], ag[i], acc[mb][m][i]));
+            for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[m][i], acc[mb][m][i]);
         }
+        if constexpr ((j & 3) == 3) bias4(g + p - 3);
       });
       // the next stage into the other buffer (its readers passed the last barrier)
       static_for<SG>([&](auto pc) __attribute__((always_inline)) {
@@ -477,6 +494,7 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
       constexpr int st = decltype(sc)::value;
       if (g0 + st * SG < G) stage(ic<st * SG>{}, g0 + st * SG);
     });
+    if (G & 3) bias4(G & ~3);  // the last partial set of four
 
 
     // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16
