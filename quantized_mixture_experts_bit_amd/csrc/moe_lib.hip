@@ -306,7 +306,7 @@ size_t fused_h_stride(const moe_shape* s) {
 struct Ws {
   size_t gu_count, dn_count, fused_sync, fused_lg, fused_h, fused_eo, fused_x, router_partial, gu_partial, h_hi,
       h_lo, h_gsum,
-      shared_part, pf_H, pf_Hs, pf_shared_out, pf_hmaxp, pf_Hh, pf_hsc, pf_xg, st_eo, st_y, total;
+      shared_part, pf_shared_out, pf_hbs, pf_Hh, pf_xg, st_eo, st_y, total;
 };
 Ws ws_layout(const moe_shape* s, int rows) {
   const DecodeCfg dc = decode_cfg(s);
@@ -334,12 +334,9 @@ Ws ws_layout(const moe_shape* s, int rows) {
   w.h_lo = take(sizeof(uint16_t) * (size_t)(k + 1) * dc.fmax);
   w.h_gsum = take(sizeof(float) * (size_t)(k + 1) * dc.nbmax);
   w.shared_part = take(sizeof(float) * (size_t)dc.Ps * d);
-  w.pf_H = take(sizeof(float) * R * k * s->d_ff);
-  w.pf_Hs = take(sizeof(float) * R * s->d_ff_shared);
   w.pf_shared_out = take(sizeof(float) * kSharedDownParts * R * d);
-  w.pf_hmaxp = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
+  w.pf_hbs = take(sizeof(float) * R * ((size_t)k * (s->d_ff / 64) + s->d_ff_shared / 64));
   w.pf_Hh = take(sizeof(uint16_t) * R * ((size_t)k * s->d_ff + s->d_ff_shared));
-  w.pf_hsc = take(sizeof(float) * R * (k + 1));
   w.pf_xg = take(sizeof(float) * R * ((d / 64 + 3) & ~3));  // rows padded to a multiple of 4 groups
   // the stacked decode's per-layer outputs the caller does not keep (layer-by-layer path)
   w.st_eo = take(sizeof(float) * (size_t)k * d);
@@ -542,13 +539,10 @@ PrefillArgs prefill_args(const moe_shape* s, const moe_layer* L, int rows, const
   const int P = rows * s->top_k;
   A.routed_mtiles = cdiv(P, 64) + std::min(s->n_experts, P);
   A.shared_mtiles = cdiv(rows, 64);
-  A.H = at<float>(ws, W.pf_H);
-  A.Hs = at<float>(ws, W.pf_Hs);
   A.expert_out = expert_out;
   A.shared_out = at<float>(ws, W.pf_shared_out);
-  A.hmaxp = at<float>(ws, W.pf_hmaxp);
+  A.hbs = at<float>(ws, W.pf_hbs);
   A.Hh = at<uint16_t>(ws, W.pf_Hh);
-  A.hsc = at<float>(ws, W.pf_hsc);
   A.xg = at<float>(ws, W.pf_xg);
   return A;
 }
@@ -599,7 +593,7 @@ int persistent_grid(int resident, int items) {
   return std::max(g, 1);
 }
 
-// one gate/up launch, the H conversion and one down launch covering the routed
+// one gate/up launch and one down launch covering the routed
 // tiles and/or the shared expert's tiles; with group_sums, first the activations'
 // group sums (when the router kernel has not left them)
 template <typename XT>
@@ -613,10 +607,6 @@ void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, bool g
   const int gu_items = xcd_blocks(A.routed_mtiles, A.f / 64) + xcd_blocks(A.shared_mtiles, A.fs / 64);
   if (gu_items == 0) return;
   k_prefill_gateup<XT><<<persistent_grid(resident_blocks(k_prefill_gateup<XT>, cap_gu), gu_items), 256, 0, st>>>(A, x);
-  const int P = A.rows * A.top_k;
-  const int first = routed ? 0 : P;
-  const int count = (routed ? P : 0) + (shared ? A.rows : 0);
-  k_prefill_hconv<<<cdiv(count, 4), 256, 0, st>>>(A, first, count);
   const int dnc = (A.d / 64 + kDownBlocks - 1) / kDownBlocks;
   const int dn_items = xcd_blocks(A.routed_mtiles, dnc) + xcd_blocks(A.shared_mtiles, dnc);
   k_prefill_down<<<persistent_grid(resident_blocks(k_prefill_down, cap_dn), dn_items), 256, 0, st>>>(A);

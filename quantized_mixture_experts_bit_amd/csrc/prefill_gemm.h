@@ -72,11 +72,10 @@ struct PrefillArgs {
   int routed_mtiles;      // upper bound of routed 64-row tiles
   int shared_mtiles;      // 64-row tiles of the shared expert
   const float* xg;        // group sums of the activations, fp32 [rows][d/64] (the router kernel's)
-  float* H;               // routed GeGLU output, fp32 [rows*top_k][f] (sorted-pair order)
-  float* Hs;              // shared GeGLU output, fp32 [rows][fs]
-  float* hmaxp;           // max |h| per (row, 64-column block): routed [rows*top_k][f/64], then shared [rows][fs/64]
-  uint16_t* Hh;           // fp16 of h * hsc: routed [rows*top_k][f], then shared [rows][fs]
-  float* hsc;             // power-of-two row scale of Hh: routed [rows*top_k], then shared [rows]
+  uint16_t* Hh;           // GeGLU output h as fp16 of h * hbs: routed [rows*top_k][f] (sorted-pair order),
+                          // then shared [rows][fs]
+  float* hbs;             // power-of-two scale of each (row, 64-column block) of Hh: routed
+                          // [rows*top_k][f/64], then shared [rows][fs/64]
   float* expert_out;      // [rows*top_k][d]
   float* shared_out;      // [kSharedDownParts][rows][d]: the shared expert's down in K parts
 };
@@ -269,6 +268,7 @@ struct GateupSmem {
   __attribute__((aligned(16))) uint16_t Xls[LO ? 2 * 64 * 72 : 8];
   __attribute__((aligned(16))) float xgL[kMaxG * 64];
   float hmL[4][64];
+  __attribute__((aligned(16))) float hsL[64];
 };
 
 // One work item = (64-row tile, 64 d_ff columns). Wave w owns d_ff columns [16w, +16)
@@ -497,27 +497,40 @@ __device__ __forceinline__ void gateup_tile(const PrefillArgs& A, const XT* __re
     if (G & 3) bias4(G & ~3);  // the last partial set of four
 
 
-    // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16
-    float* H = shared ? A.Hs : A.H;
-    float* hmaxp = shared ? A.hmaxp + (size_t)A.rows * A.top_k * (A.f / 64) : A.hmaxp;
+    // GeGLU epilogue: lane holds rows 16mb + 4*(lane/16) + i, d_ff column fc*64 + 16*wave + lane%16.
+    // h goes out as fp16, scaled per (row, 64-column block) by the power of two that brings
+    // the block's largest |h| into [2^14, 2^15); the scale goes out beside it (the down
+    // kernel brings a row's blocks to one scale as it stages them).
+    uint16_t* Hh = shared ? A.Hh + (size_t)A.rows * A.top_k * A.f : A.Hh;
+    float* hbs = shared ? A.hbs + (size_t)A.rows * A.top_k * (A.f / 64) : A.hbs;
     const int F = T.F, nG = F / 64;
+    float hv[NMB][4];
   #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
   #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mb + 4 * (lane >> 4) + i;
-        float h = 0.0f;
-        if (r < T.mrows) {
-          h = gelu_tanh(acc[mb][0][i]) * acc[mb][1][i];
-          H[(size_t)(T.m0 + r) * F + fc * 64 + 16 * wave + (lane & 15)] = h;
-        }
+        hv[mb][i] = r < T.mrows ? gelu_tanh(acc[mb][0][i]) * acc[mb][1][i] : 0.0f;
         // max |h| over the 16 lanes holding this row: one DPP row (VALU, no LDS round trips)
-        const float mx = row16_max(fabsf(h));
+        const float mx = row16_max(fabsf(hv[mb][i]));
         if ((lane & 15) == 0) hmL[wave][r] = mx;
       }
     __syncthreads();
-    if (tid < T.mrows)
-      hmaxp[(size_t)(T.m0 + tid) * nG + fc] = fmaxf(fmaxf(hmL[0][tid], hmL[1][tid]), fmaxf(hmL[2][tid], hmL[3][tid]));
+    if (tid < 64) {
+      const float sc = row_scale(fmaxf(fmaxf(hmL[0][tid], hmL[1][tid]), fmaxf(hmL[2][tid], hmL[3][tid])));
+      S.hsL[tid] = sc;
+      if (tid < T.mrows) hbs[(size_t)(T.m0 + tid) * nG + fc] = sc;
+    }
+    __syncthreads();
+  #pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(&S.hsL[16 * mb + 4 * (lane >> 4)]);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mb + 4 * (lane >> 4) + i;
+        if (r < T.mrows) Hh[(size_t)(T.m0 + r) * F + fc * 64 + 16 * wave + (lane & 15)] = f16_bits(hv[mb][i] * sc[i]);
+      }
+    }
 
   };
   if (nmb == 1)
@@ -560,61 +573,6 @@ __global__ __launch_bounds__(256, 2) void k_prefill_gateup(PrefillArgs A, const 
   }
 }
 
-// ---------------------------------------------------------------- H to fp16
-
-// One wavefront per H row (rows [first, first + count) of the routed rows followed
-// by the shared rows): the row's power-of-two scale from its per-block maxima, then
-// the fp16 copy of h * scale. Every load of a round (the maxima and up to
-// kHconvLoads 16-byte pieces of the row per lane) is issued before any is used.
-constexpr int kHconvLoads = 9;
-__global__ __launch_bounds__(256) void k_prefill_hconv(PrefillArgs A, int first, int count) {
-  const int lane = threadIdx.x & 63;
-  const int r = first + (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (r >= first + count) return;
-  const int P = A.rows * A.top_k;
-  const float* src;
-  const float* mp;
-  uint16_t* dst;
-  int F;
-  if (r < P) {
-    F = A.f;
-    src = A.H + (size_t)r * F;
-    mp = A.hmaxp + (size_t)r * (F / 64);
-    dst = A.Hh + (size_t)r * F;
-  } else {
-    const int rs = r - P;
-    F = A.fs;
-    src = A.Hs + (size_t)rs * F;
-    mp = A.hmaxp + (size_t)P * (A.f / 64) + (size_t)rs * (F / 64);
-    dst = A.Hh + (size_t)P * A.f + (size_t)rs * F;
-  }
-  const int nG = F / 64;
-  const rsrc_t hres = buf_rsrc(src, (uint32_t)F * 4u);  // loads past the row return 0
-  float m = 0.0f;
-  for (int c0 = 0; c0 < F; c0 += 256 * kHconvLoads) {
-    u32x4_t v[kHconvLoads];
-#pragma unroll
-    for (int j = 0; j < kHconvLoads; ++j) v[j] = bld16(hres, (uint32_t)(c0 + 256 * j + 4 * lane) * 4u, 0);
-    if (c0 == 0) {
-      for (int i = lane; i < nG; i += 64) m = fmaxf(m, mp[i]);
-      m = wave_fmax(m);
-    }
-    const float sc = row_scale(m);
-    if (c0 == 0 && lane == 0) A.hsc[r] = sc;
-#pragma unroll
-    for (int j = 0; j < kHconvLoads; ++j) {
-      const int c = c0 + 256 * j + 4 * lane;
-      if (c < F) {
-        const uint32_t p0 = (uint32_t)f16_bits(__uint_as_float(v[j][0]) * sc) |
-                            ((uint32_t)f16_bits(__uint_as_float(v[j][1]) * sc) << 16);
-        const uint32_t p1 = (uint32_t)f16_bits(__uint_as_float(v[j][2]) * sc) |
-                            ((uint32_t)f16_bits(__uint_as_float(v[j][3]) * sc) << 16);
-        *reinterpret_cast<uint2*>(dst + c) = make_uint2(p0, p1);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- down
 
 struct DownSmem {
@@ -642,7 +600,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   const int nmb = (T.mrows + 15) >> 4;
   const int P = A.rows * A.top_k;
   const uint16_t* Hh = shared ? A.Hh + (size_t)P * A.f : A.Hh;
-  const float* hsc = shared ? A.hsc + P : A.hsc;
+  const float* hbs = shared ? A.hbs + (size_t)P * (A.f / 64) : A.hbs;
 
   const int wrow = 16 * wave + (lane & 15);
   const int nblk = A.d / 64;
@@ -655,33 +613,60 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
                                mstride + (uint32_t)G * kTile4);
   BRing B;
   B.init(wrow, lane, mstride);
-  if (tid < 64) rowinv[tid] = tid < T.mrows ? 1.0f / hsc[T.m0 + tid] : 1.0f;  // exact: powers of two
 
   // H staging: thread -> tile row tid/4, 16 halfs at column (tid%4)*16; rows past
   // the tile's end repeat its first row (see the gate/up kernel)
   const int hr = tid >> 2, hq = tid & 3;
+  const int hrow = T.m0 + (hr < T.mrows ? hr : 0);
   const rsrc_t hres = buf_rsrc(Hh, (uint32_t)((size_t)(shared ? A.rows : P) * F * sizeof(uint16_t)));
-  const uint32_t hvo = (uint32_t)(((size_t)(T.m0 + (hr < T.mrows ? hr : 0)) * F + hq * 16) * sizeof(uint16_t));
+  const uint32_t hvo = (uint32_t)(((size_t)hrow * F + hq * 16) * sizeof(uint16_t));
+  // the row's scale in this item: the smallest of its blocks' scales over [gb, ge) (that
+  // of its largest block), as the exponent field of the power of two; each staged block
+  // is brought to it by an exact power-of-two product (at most 1), and the outputs are
+  // divided by it at the end
+  const rsrc_t sres = buf_rsrc(hbs, (uint32_t)((size_t)(shared ? A.rows : P) * G * sizeof(float)));
+  const uint32_t svo = (uint32_t)((size_t)hrow * G * sizeof(float));
+  uint32_t emin = 255u;
+  for (int g0 = gb; g0 < ge; g0 += 8) {
+    uint32_t sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = bld4(sres, svo + (uint32_t)min(g0 + j, ge - 1) * 4u, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) emin = min(emin, (sv[j] >> 23) & 0xffu);
+  }
+  if (hq == 0) rowinv[hr] = 1.0f / __uint_as_float(emin << 23);  // exact: a power of two
   u32x4_t ha[RA][2];
+  uint32_t hs[RA];
   auto aload = [&](auto sc, int g) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
     const uint32_t so = (uint32_t)(g * kGroup * sizeof(uint16_t));
     ha[slot][0] = bld16(hres, hvo, so);
     ha[slot][1] = bld16(hres, hvo + 16, so);
+    hs[slot] = bld4(sres, svo + (uint32_t)g * 4u, 0);
   };
   // the staging threads also add up each row's group (dot products against fp16 (1, 1)
   // pairs, the four threads of a row summed by DPP) for the bias term of the epilogue
   auto astore = [&](auto sc, int buf) __attribute__((always_inline)) {
     constexpr int slot = decltype(sc)::value;
+    // 2^(emin - e) for this block's exponent e: the fp16 product rounds only below the
+    // fp16 normal range (values 2^-28 of the row's largest or smaller)
+    const uint32_t m1 = f16_bits(ldexpf(1.0f, (int)emin - (int)((hs[slot] >> 23) & 0xffu)));
+    const f16x2_t m2 = __builtin_bit_cast(f16x2_t, m1 | (m1 << 16));
+    u32x4_t hv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        hv[h][c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, (uint32_t)ha[slot][h][c]) * m2);
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(&Hl[buf][hr * kLdsStride + hq * 16]);
-    dst[0] = ha[slot][0];
-    dst[1] = ha[slot][1];
+    dst[0] = hv[0];
+    dst[1] = hv[1];
     float v = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t w = ha[slot][h][c];  // a bit_cast of the vector element itself reads element 0
+        const uint32_t w = hv[h][c];  // a bit_cast of the vector element itself reads element 0
         v = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3C003C00u), v, false);
       }
     v = dpp_add<0xB1, 0xf>(v);  // the four threads of a row are one quad
