@@ -626,15 +626,12 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   // divided by it at the end
   const rsrc_t sres = buf_rsrc(hbs, (uint32_t)((size_t)(shared ? A.rows : P) * G * sizeof(float)));
   const uint32_t svo = (uint32_t)((size_t)hrow * G * sizeof(float));
+  // (the first 16 groups' scales in one batch of loads, in flight with the prologue's)
   uint32_t emin = 255u;
-  for (int g0 = gb; g0 < ge; g0 += 8) {
-    uint32_t sv[8];
+  uint32_t sv[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = bld4(sres, svo + (uint32_t)min(g0 + j, ge - 1) * 4u, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) emin = min(emin, (sv[j] >> 23) & 0xffu);
-  }
-  if (hq == 0) rowinv[hr] = 1.0f / __uint_as_float(emin << 23);  // exact: a power of two
+  for (int j = 0; j < 16; ++j) sv[j] = bld4(sres, svo + (uint32_t)min(gb + j, ge - 1) * 4u, 0);
+  for (int g = gb + 16; g < ge; ++g) emin = min(emin, (bld4(sres, svo + (uint32_t)g * 4u, 0) >> 23) & 0xffu);
   u32x4_t ha[RA][2];
   uint32_t hs[RA];
   auto aload = [&](auto sc, int g) __attribute__((always_inline)) {
@@ -688,6 +685,9 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     B.load(jc, wres, min(gb + j, ge - 1));
     if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(gb + j + 1, ge - 1));
     if constexpr (j + 1 == RA) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) emin = min(emin, (sv[t] >> 23) & 0xffu);
+      if (hq == 0) rowinv[hr] = 1.0f / __uint_as_float(emin << 23);  // exact: a power of two
       astore(ic<0>{}, 0);
       aload(ic<0>{}, min(gb + RA, ge - 1));
     }
