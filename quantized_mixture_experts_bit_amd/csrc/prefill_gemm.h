@@ -210,7 +210,7 @@ __device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
 }
 
 // Weight fragments of two 64-row blocks (gate and up of one column block, or two output
-// blocks of the down projection) in a ring of kRing groups, for wave row `row` (0..63
+// blocks of the down projection) in a ring of kDepth groups, for wave row `row` (0..63
 // within a block). The matrix cores want, in lane 16c + n, code word c of row n's 16-byte
 // segment of each (block, k-half). Those words sit 16 bytes apart, so fetching them
 // directly takes four 4-byte loads whose 16-lane quarters each touch 256 bytes. Instead
@@ -221,9 +221,10 @@ __device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
 // row, and one permlane16 swap of that register with itself puts block 0's word in every
 // row of one result and block 1's in every row of the other. One buffer resource spans
 // both blocks, which start `mstride` bytes apart; the group enters as a scalar offset.
-struct BRing {
-  u32x4_t cw[kRing];  // as fetched; transposed when used
-  uint32_t sb[kRing];
+template <int kDepth>
+struct BRingT {
+  u32x4_t cw[kDepth];  // as fetched; transposed when used
+  uint32_t sb[kDepth];
   uint32_t vc, vs;
   __device__ __forceinline__ void init(int row, int lane, uint32_t mstride) {
     vc = (uint32_t)(lane >> 5) * mstride + (uint32_t)((lane >> 4) & 1) * 1024u + (uint32_t)row * 16u;
@@ -252,6 +253,7 @@ struct BRing {
     return u32x4_t{c[0], c[1], d[0], d[1]};
   }
 };
+using BRing = BRingT<kRing>;
 
 __device__ __forceinline__ void zero_acc(f32x4_t& a) { a = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
@@ -581,14 +583,16 @@ struct DownSmem {
   __attribute__((aligned(16))) float agL[2][64];  // per-row sums of the staged H group
 };
 
-// One work item = (64-row tile, two blocks of 64 output columns, 2 np and 2 np + 1).
-// Wave w owns output columns [16w, +16) of both blocks for every row of the tile, so
-// one staged H tile feeds twice the columns. With an odd number of blocks the last
-// item's second block repeats its first and is not stored.
-constexpr int kDownBlocks = 2;
+// One work item = (64-row tile, four blocks of 64 output columns, 4 np .. 4 np + 3).
+// Wave w owns output columns [16w, +16) of every block for every row of the tile, so
+// one staged H tile feeds four times the columns, and a 128-row chunk's items fit the
+// chip's resident workgroups in one round. The weights come in two rings of two blocks
+// each, two groups deep. Blocks past the last one repeat it and are not stored.
+constexpr int kDownBlocks = 4;
+constexpr int kDownRing = 2;  // weight groups in flight per ring
 __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, int np, bool shared, int part,
                                           DownSmem& S) {
-  constexpr int RA = 4;
+  constexpr int RA = 2;  // H groups in flight
   auto& Hl = S.Hl;
   auto& rowinv = S.rowinv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -604,15 +608,20 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
 
   const int wrow = 16 * wave + (lane & 15);
   const int nblk = A.d / 64;
-  static_assert(kDownBlocks == 2, "the weight ring holds two blocks");
+  static_assert(kDownBlocks == 4, "two weight rings of two blocks each");
+  static_assert(4 % kDownRing == 0, "the unrolled steps cover whole ring passes");
   int nbm[kDownBlocks];
 #pragma unroll
   for (int m = 0; m < kDownBlocks; ++m) nbm[m] = min(kDownBlocks * np + m, nblk - 1);
-  const uint32_t mstride = (uint32_t)(nbm[1] - nbm[0]) * G * kTile4;  // 0 for a repeated last block
-  const rsrc_t wres = buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nbm[0] * G * kTile4,
-                               mstride + (uint32_t)G * kTile4);
-  BRing B;
-  B.init(wrow, lane, mstride);
+  rsrc_t wres[2];
+  BRingT<kDownRing> B[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t mstride = (uint32_t)(nbm[2 * p + 1] - nbm[2 * p]) * G * kTile4;  // 0 for a repeated block
+    wres[p] = buf_rsrc(uniform_ptr(T.blob) + 2 * m4_bytes(F, A.d) + (uint64_t)nbm[2 * p] * G * kTile4,
+                       mstride + (uint32_t)G * kTile4);
+    B[p].init(wrow, lane, mstride);
+  }
 
   // H staging: thread -> tile row tid/4, 16 halfs at column (tid%4)*16; rows past
   // the tile's end repeat its first row (see the gate/up kernel)
@@ -680,9 +689,12 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
   // prologue: the loads in the order the steady state issues them (weights of group
   // j, then activations of group j + 1), so the wait counts agree on entry
   aload(ic<0>{}, gb);
-  static_for<kRing>([&](auto jc) __attribute__((always_inline)) {
+  static_for<RA>([&](auto jc) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
-    B.load(jc, wres, min(gb + j, ge - 1));
+    if constexpr (j < kDownRing) {
+      B[0].load(jc, wres[0], min(gb + j, ge - 1));
+      B[1].load(jc, wres[1], min(gb + j, ge - 1));
+    }
     if constexpr (j + 1 < RA) aload(ic<j + 1>{}, min(gb + j + 1, ge - 1));
     if constexpr (j + 1 == RA) {
 #pragma unroll
@@ -700,35 +712,41 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
 #pragma unroll
     for (int m = 0; m < kDownBlocks; ++m) zero_acc(acc[mb][m]);
 
-  // one K group, as in the gate/up kernel
+  // one K group, as in the gate/up kernel (H slot j of RA, weight slot j % kDownRing);
+  // one ring's two blocks at a time, so only their operands are live
   const NibKT<0x64006400u> nk;
   auto step = [&](auto jc, int g) __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     constexpr int buf = j & 1;
-    f16x8_t b0[kDownBlocks], b1[kDownBlocks];
-    float s[kDownBlocks], bp[kDownBlocks];
-    const u32x4_t cw = B.codes(jc);
-    const u32x2_t sbw = B.scales(jc);
+    constexpr int ws = j % kDownRing;
 #pragma unroll
-    for (int m = 0; m < kDownBlocks; ++m) {
-      b0[m] = codes_f16(cw[2 * m], nk);
-      b1[m] = codes_f16(cw[2 * m + 1], nk);
-      s[m] = bf16_lo(sbw[m]);
-      bp[m] = bf16_hi(sbw[m]);
-    }
-    B.load(jc, wres, min(g + kRing, ge - 1));
+    for (int p = 0; p < 2; ++p) {
+      f16x8_t b0[2], b1[2];
+      float s[2], bp[2];
+      const u32x4_t cw = B[p].codes(ic<ws>{});
+      const u32x2_t sbw = B[p].scales(ic<ws>{});
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb < nmb) {
-        const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
-        const f16x8_t a0 = lds_frag<f16x8_t>(&Hl[buf][ao]);
-        const f16x8_t a1 = lds_frag<f16x8_t>(&Hl[buf][ao + 32]);
-        const f32x4_t ag = *reinterpret_cast<const f32x4_t*>(&S.agL[buf][16 * mb + 4 * (lane >> 4)]);
+      for (int h = 0; h < 2; ++h) {
+        b0[h] = codes_f16(cw[2 * h], nk);
+        b1[h] = codes_f16(cw[2 * h + 1], nk);
+        s[h] = bf16_lo(sbw[h]);
+        bp[h] = bf16_hi(sbw[h]);
+      }
+      B[p].load(ic<ws>{}, wres[p], min(g + kDownRing, ge - 1));
 #pragma unroll
-        for (int m = 0; m < kDownBlocks; ++m) {
-          const f32x4_t t = mfma(a1, b1[m], mfma(a0, b0[m], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb < nmb) {
+          const int ao = (16 * mb + (lane & 15)) * kLdsStride + 8 * (lane >> 4);
+          const f16x8_t a0 = lds_frag<f16x8_t>(&Hl[buf][ao]);
+          const f16x8_t a1 = lds_frag<f16x8_t>(&Hl[buf][ao + 32]);
+          const f32x4_t ag = *reinterpret_cast<const f32x4_t*>(&S.agL[buf][16 * mb + 4 * (lane >> 4)]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mb][m][i] = fmaf(s[m], t[i], fmaf(bp[m], ag[i], acc[mb][m][i]));
+          for (int h = 0; h < 2; ++h) {
+            const f32x4_t t = mfma(a1, b1[h], mfma(a0, b0[h], f32x4_t{0.f, 0.f, 0.f, 0.f}));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[mb][2 * p + h][i] = fmaf(s[h], t[i], fmaf(bp[h], ag[i], acc[mb][2 * p + h][i]));
+          }
         }
       }
     }
@@ -737,15 +755,12 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
     __syncthreads();
   };
   int g0 = gb;
-  for (; g0 + kRing <= ge; g0 += kRing) {
+  static_assert(RA == 2 && kDownRing == 2, "the loop below is unrolled over two H and weight slots");
+  for (; g0 + RA <= ge; g0 += RA) {
     step(ic<0>{}, g0);
     step(ic<1>{}, g0 + 1);
-    step(ic<2>{}, g0 + 2);
-    step(ic<3>{}, g0 + 3);
   }
   if (g0 < ge) step(ic<0>{}, g0);
-  if (g0 + 1 < ge) step(ic<1>{}, g0 + 1);
-  if (g0 + 2 < ge) step(ic<2>{}, g0 + 2);
 #pragma unroll
   for (int m = 0; m < kDownBlocks; ++m) {
     if (kDownBlocks * np + m >= nblk) break;  // the repeated last block
