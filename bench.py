@@ -75,12 +75,19 @@ CSRC = os.path.join(ROOT, "quantized_mixture_experts_bit_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_fused_gemma4_decode_traffic.txt")
 
 
-def csrc_digest():
-    """sha256 over the HIP sources (names and bytes, sorted): identifies the kernel build."""
+# the files k_decode_fused is built and launched from (its counters stay valid while these do)
+DECODE_KERNEL_SOURCES = ("common.h", "decode_fused.h", "moe_lib.hip")
+
+
+def csrc_digest(names=None):
+    """sha256 over the HIP sources (names and bytes, sorted), or over `names` only:
+    identifies the kernel build."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         p = os.path.join(CSRC, name)
+        if names is not None and name not in names:
+            continue
         if os.path.isfile(p) and name.endswith((".h", ".hip", ".cpp")):
             h.update(name.encode())
             with open(p, "rb") as f:
@@ -91,7 +98,7 @@ def csrc_digest():
 def measured_traffic():
     """HBM bytes per k_decode_fused launch from the committed counter summary (FETCH_SIZE and
     WRITE_SIZE passes, each divided by the factor the same counter shows on a plain copy of
-    known size), or None when the summary is missing or the kernel sources changed since."""
+    known size), or None when the summary is missing or the kernel's sources changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None, None
     kv = {}
@@ -100,7 +107,7 @@ def measured_traffic():
             if ":" in line and not line.startswith("#"):
                 a, b = line.split(":", 1)
                 kv[a.strip()] = b.strip()
-    if kv.get("csrc_sha256") != csrc_digest():
+    if kv.get("decode_sources_sha256") != csrc_digest(DECODE_KERNEL_SOURCES):
         return None, "counters were taken on other kernel sources"
     fetch = float(kv["fetch_bytes_per_launch"]) / float(kv["copy_factor_fetch"])
     write = float(kv["write_bytes_per_launch"]) / float(kv["copy_factor_write"])
