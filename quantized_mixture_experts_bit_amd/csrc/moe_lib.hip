@@ -608,7 +608,8 @@ void launch_prefill(PrefillArgs A, const XT* x, bool routed, bool shared, bool g
   if (gu_items == 0) return;
   k_prefill_gateup<XT><<<persistent_grid(resident_blocks(k_prefill_gateup<XT>, cap_gu), gu_items), 256, 0, st>>>(A, x);
   const int dnc = (A.d / 64 + kDownBlocks - 1) / kDownBlocks;
-  const int dn_items = xcd_blocks(A.routed_mtiles, dnc) + xcd_blocks(A.shared_mtiles, dnc);
+  // (the shared expert's down runs in kSharedDownParts K parts per row tile)
+  const int dn_items = xcd_blocks(A.routed_mtiles, dnc) + xcd_blocks(A.shared_mtiles * kSharedDownParts, dnc);
   k_prefill_down<<<persistent_grid(resident_blocks(k_prefill_down, cap_dn), dn_items), 256, 0, st>>>(A);
 }
 
