@@ -2,8 +2,8 @@
 // against that expert's weights, one fetch of a weight tile serving every row of
 // the workgroup's row tile.
 //   gate/up: [rows_e x d] x [d x 2*f] on v_mfma_f32_16x16x32_bf16, GeGLU in the
-//            epilogue, H_e kept in fp32 [rows_e x f];
-//   H pass:  each H row scaled by a power of two and rounded to fp16;
+//            epilogue, H_e stored as fp16 [rows_e x f], each (row, 64-column block)
+//            scaled by a power of two kept beside it;
 //   down:    [rows_e x f] x [f x d] on v_mfma_f32_16x16x32_f16, fp32 output per
 //            (row, slot) pair.
 //
@@ -17,9 +17,10 @@
 // Codes and activations enter exactly:
 //   gate/up: x is bf16 (exact; fp32 x is split into two bf16 terms hi + lo),
 //            c_i = 128 + q_i as bf16 from one mask-and-or per code pair (c0 = 128);
-//   down:    H rows scaled so their largest |h| lands in [2^14, 2^15) and rounded
-//            to fp16 (11 bits), c_i = q_i as exact fp16 (c0 = 0), and the
-//            scale divided out at the end (exactly: a power of two).
+//   down:    H blocks scaled so their largest |h| lands in [2^14, 2^15), rounded to
+//            fp16 (11 bits) and brought to one scale per row and item (exact powers
+//            of two), c_i = 1024 + q_i as exact fp16 from one mask-and-or per code
+//            pair (c0 = 1024), and the scale divided out at the end (exactly).
 //
 // Each wavefront loads its own weight fragments straight from the packed tiles
 // (the tile layout gives lane l the code word of row l%16, columns 8*(l/16)..+7)
@@ -186,14 +187,13 @@ __device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w, const NibK& nk) {
   return __builtin_bit_cast(bf16x8_t, p);
 }
 
-// B operand, down: the 8 codes of one packed word as exact fp16 values q (0..15):
-// the pair (1024 + q, 1024 + q') is built with a mask and an OR of the exponent of
-// 1024 (0x6400), then 1024 is subtracted with one packed fp16 add per pair.
+// B operand, down: the 8 codes of one packed word as exact fp16 values 1024 + q: each
+// pair (1024 + q, 1024 + q') is a mask and an OR of the exponent of 1024 (0x6400), and
+// 1024 goes into the bias term (b - 1024 s), as in the decode GEMV.
 __device__ __forceinline__ f16x8_t codes_f16(uint32_t w, const NibKT<0x64006400u>& mk) {
-  const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   f16x2_t p[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) p[t] = __builtin_bit_cast(f16x2_t, ((w >> (4 * t)) & mk.mask) | mk.expo) - k1024;
+  for (int t = 0; t < 4; ++t) p[t] = __builtin_bit_cast(f16x2_t, ((w >> (4 * t)) & mk.mask) | mk.expo);
   return f16x8_t{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
@@ -730,7 +730,7 @@ __device__ __forceinline__ void down_tile(const PrefillArgs& A, const MTile& T, 
         b0[h] = codes_f16(cw[2 * h], nk);
         b1[h] = codes_f16(cw[2 * h + 1], nk);
         s[h] = bf16_lo(sbw[h]);
-        bp[h] = bf16_hi(sbw[h]);
+        bp[h] = fmaf(-1024.0f, s[h], bf16_hi(sbw[h]));  // b - 1024 s (exact)
       }
       B[p].load(ic<ws>{}, wres[p], min(g + kDownRing, ge - 1));
 #pragma unroll
